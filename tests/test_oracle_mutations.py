@@ -1,0 +1,129 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case swaps one oracle function for a plausible wrong version and asserts
+that the corresponding pin check fails.  This shows the pins are not vacuous.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_oracle as mo
+from tests import test_oracle_method as pins
+from tests import test_oracle_formats as fmt
+
+F32 = np.float32
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(mo, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _select_group_max_always(s, bias, n_groups, topk_groups, topk):
+    # mistake: group score = max even when a bias exists
+    T, E = s.shape
+    sp = (s + bias).astype(F32) if bias is not None else s
+    g = E // n_groups
+    idx = np.empty((T, topk), np.int32)
+    for t in range(T):
+        row = sp[t]
+        if n_groups > 1:
+            gs = row.reshape(n_groups, g).max(1)
+            keep = np.argsort(-gs, kind="stable")[:topk_groups]
+            cand = np.concatenate([np.arange(k * g, (k + 1) * g) for k in keep])
+        else:
+            cand = np.arange(E)
+        idx[t] = cand[np.argsort(-row[cand], kind="stable")[:topk]]
+    return idx, {"margin_group": np.full(T, np.inf), "margin_expert": np.full(T, np.inf)}
+
+
+def test_group_score_mistake_is_caught(monkeypatch):
+    _patch(monkeypatch, "select_experts", _select_group_max_always)
+    with pytest.raises(AssertionError):
+        pins.check_select_vs_brute_force(seed=0)
+
+
+def test_weights_from_biased_scores_is_caught(monkeypatch):
+    orig = mo.routing_weights
+
+    def biased(s, idx, func, rs):
+        # mistake: weights gathered from s + bias (the pin's forcing bias: 10 on expert 5)
+        b = np.zeros(s.shape[1], F32)
+        b[5] = 10.0
+        return orig((s + b).astype(F32), idx, func, rs)
+    _patch(monkeypatch, "routing_weights", biased)
+    with pytest.raises(AssertionError):
+        pins.check_bias_selects_only()
+
+
+def test_missing_renormalisation_is_caught(monkeypatch):
+    def no_renorm(s, idx, func, rs):
+        w = np.take_along_axis(s, idx.astype(np.int64), 1)
+        return (w * F32(rs)).astype(F32)
+    _patch(monkeypatch, "routing_weights", no_renorm)
+    s = oracle.scores(np.random.default_rng(0).standard_normal((10, 16)).astype(F32), "sigmoid")
+    idx, _ = oracle.select_experts(s, None, 4, 2, 4)
+    with pytest.raises(AssertionError):
+        pins.check_weight_invariants(s, idx, oracle.routing_weights(s, idx, "sigmoid", 2.5),
+                                     "sigmoid", 2.5)
+
+
+def test_renormalising_softmax_is_caught(monkeypatch):
+    def renorm_all(s, idx, func, rs):
+        w = np.take_along_axis(s, idx.astype(np.int64), 1)
+        return (w / w.sum(1, keepdims=True) * F32(rs)).astype(F32)
+    _patch(monkeypatch, "routing_weights", renorm_all)
+    s = oracle.scores(np.random.default_rng(0).standard_normal((10, 16)).astype(F32), "softmax")
+    idx, _ = oracle.select_experts(s, None, 1, 1, 3)
+    with pytest.raises(AssertionError):
+        pins.check_weight_invariants(s, idx, oracle.routing_weights(s, idx, "softmax", 1.0),
+                                     "softmax", 1.0)
+
+
+def test_descending_permutation_is_caught():
+    rng = np.random.default_rng(4)
+    idx = np.stack([rng.choice(16, 4, replace=False) for _ in range(30)]).astype(np.int32)
+    counts, offsets, st, ro = oracle.permute(idx, 16)
+    # mistake: tokens in descending order inside each expert segment
+    st2, ro2 = st.copy(), ro.copy()
+    for e in range(16):
+        a, b = offsets[e], offsets[e + 1]
+        seg = st[a:b][::-1].copy()
+        st2[a:b] = seg
+        for j, t in enumerate(seg):
+            k = int(np.nonzero(idx[t] == e)[0][0])
+            ro2[t, k] = a + j
+    with pytest.raises(AssertionError):
+        pins.check_permute(idx, 16, counts, offsets, st2, ro2)
+
+
+def test_swapped_swiglu_branches_is_caught(monkeypatch):
+    monkeypatch.setattr(mo, "swiglu", lambda a1, a3: mo.silu(a3) * a1)
+    with pytest.raises(AssertionError):
+        pins.test_ffn_hand_example()
+
+
+def test_dropped_shared_expert_is_caught(monkeypatch):
+    orig = mo.moe_forward
+
+    def no_shared(*a, **k):
+        a = list(a)
+        a[4] = None
+        return orig(*a, **k)
+    monkeypatch.setattr(mo, "moe_forward", no_shared)
+    monkeypatch.setattr(oracle, "moe_forward", no_shared)
+    with pytest.raises(AssertionError):
+        pins.test_identical_experts_closed_form()
+
+
+def test_ties_away_from_zero_is_caught(monkeypatch):
+    orig = mo.e4m3_encode
+
+    def away(v):
+        v = np.asarray(v, np.float64)
+        return orig(v + np.sign(v) * np.abs(v) * 1e-12)     # nudges exact ties upward
+    monkeypatch.setattr(mo, "e4m3_encode", away)
+    monkeypatch.setattr(oracle, "e4m3_encode", away)
+    with pytest.raises(AssertionError):
+        fmt.test_e4m3_midpoints_round_to_even_code()
