@@ -1,0 +1,202 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--no-cpu-baseline]
+
+One step = one moe_forward call (gate, dispatch, routed + shared SwiGLU
+experts, combine) over one batch of T synthetic tokens, with inputs and
+weights already resident in HBM.  Prints one JSON line.
+
+roofline: the dominant kernel is the up-projection grouped GEMM (it streams
+W1 and W3 of every expert that receives a token, two thirds of the layer's
+weight bytes).  Its algorithmic bytes per launch divided by its average
+launch time (HIP events recorded around that launch on its own stream during
+the timed steps) against the MI355X HBM peak of 8 TB/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+METRIC = "MoE-layer tokens/sec, DeepSeek-V3 shape T=4096 bf16 + T=128 decode; % MFMA/HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--also", default="c2", help="extra configs timed after the main one ('' = none)")
+    return ap.parse_args()
+
+
+def workload_numbers(cfg, counts):
+    """Algorithmic FLOPs and bytes of one forward, and of the up-projection launch."""
+    wsz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w_dtype]
+    asz = 4 if cfg.act_dtype == "f32" else 2
+    rsz = 4 if cfg.router_dtype == "f32" else 2
+    T, dim, E, K, I, Is = cfg.T, cfg.dim, cfg.E, cfg.topk, cfg.inter, cfg.inter_shared
+    active = int((counts > 0).sum())
+    scale_b = 0
+    if cfg.w_dtype == "fp8":
+        scale_b = 4 * (dim // 128) * (I // 128)          # per matrix per expert
+    per_expert = 3 * (I * dim * wsz + scale_b)
+    shared = 3 * Is * dim * wsz + (3 * 4 * (dim // 128) * (Is // 128) if cfg.w_dtype == "fp8" else 0)
+    flops = 2 * T * E * dim + 2 * T * K * 3 * dim * I + 2 * T * 3 * dim * Is
+    bytes_ = active * per_expert + shared + E * dim * rsz + T * dim * asz * 2
+    hsz = 1 if cfg.w_dtype == "fp8" else asz
+    up_bytes = (active * 2 * (I * dim * wsz + scale_b) + 2 * (Is * dim * wsz) + T * dim * asz
+                + (T * K * I + T * Is) * hsz)
+    up_flops = 2 * T * K * 2 * dim * I + 2 * T * 2 * dim * Is
+    return dict(active_experts=active, flops=flops, bytes=bytes_, up_bytes=up_bytes,
+                up_flops=up_flops, per_expert_up_bytes=2 * (I * dim * wsz + scale_b))
+
+
+def traffic_for(kernel, workload):
+    """HBM traffic from the committed rocprofv3 counter runs, if the kernel
+    source is unchanged since they were taken (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "mixture_experts_layer_11_amd", "csrc", "ffn.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    ent = rec.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False):
+    layer = inputs.draw_layer(cfg)
+    dw = moe.upload_layer(layer)
+    p = moe.Params.from_config(cfg)
+    ws = moe.alloc_workspace(p, cfg.T)
+    x = moe.to_device(layer.x, cfg.act_dtype)
+    y = torch.empty((cfg.T, cfg.dim), dtype=p.act_torch, device="cuda")
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
+    torch.cuda.synchronize()
+    moe.moe_profile_start(steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(steps):
+        moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ncalls, up_ms, dn_ms = moe.moe_profile_stop()
+    ms = t0.elapsed_time(t1) / steps
+    c = counts.cpu().numpy()
+    res = dict(ms=ms, wall_ms=wall * 1e3 / steps, up_ms=up_ms / max(ncalls, 1),
+               down_ms=dn_ms / max(ncalls, 1), counts=c, **workload_numbers(cfg, c))
+    if not want_layer:
+        del dw, ws, x, y
+        torch.cuda.empty_cache()
+        return res, None
+    return res, layer
+
+
+def cpu_baseline(layer, ntok):
+    import oracle
+    from threadpoolctl import threadpool_info
+    cfg = layer.cfg
+    tokens = np.arange(ntok)
+
+    def ew(e):
+        w = layer.expert(e)
+        return w.w1, w.w3, w.w2, w.w1_s, w.w3_s, w.w2_s
+    s = layer.shared
+    sh = None if s is None else (s.w1, s.w3, s.w2, s.w1_s, s.w3_s, s.w2_s)
+    t = time.perf_counter()
+    oracle.moe_forward(layer.x, layer.wr, layer.bias, ew, sh, tokens=tokens,
+                       act_dtype=cfg.act_dtype, w_dtype=cfg.w_dtype, router_dtype=cfg.router_dtype,
+                       E=cfg.E, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, topk=cfg.topk,
+                       score_func=cfg.score_func, route_scale=cfg.route_scale)
+    dt = time.perf_counter() - t
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {ntok} of the {cfg.T} tokens of {cfg.name} (gate, their routed "
+                      f"experts and the shared expert), {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no "
+              "multi-GPU path: the layer is measured on one MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_layer_11_amd import inputs, moe
+    moe.lib()
+    cfg = inputs.config_by_name(a.config)
+    res, layer = run_config(cfg, a.steps, a.warmup, torch, moe, inputs, want_layer=True)
+    tok_s = cfg.T / (res["ms"] / 1e3)
+    up_gbs = res["up_bytes"] / (res["up_ms"] / 1e3) / 1e9
+    traffic = traffic_for("up_grouped_gemm", cfg.name)
+    roof = {"bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "up_skinny_kernel (up-projection grouped GEMM)",
+            "kernel_ms": round(res["up_ms"], 4),
+            "alg_bytes_per_launch": int(res["up_bytes"])}
+    layer_gbs = res["bytes"] / (res["ms"] / 1e3) / 1e9
+    dt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+    layer_tfs = res["flops"] / (res["ms"] / 1e3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dt, "data": "synthetic (seeded; random-init weights of the layer shape)",
+        "config": {"workload": cfg.name, "T": cfg.T, "dim": cfg.dim, "n_experts": cfg.E,
+                   "topk": cfg.topk, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
+                   "inter": cfg.inter, "shared_inter": cfg.inter_shared,
+                   "active_experts": res["active_experts"]},
+        "roofline": roof,
+        "layer": {"hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(layer_tfs / MFMA_PEAK_TFLOPS[dt], 4),
+                  "alg_bytes": int(res["bytes"]), "alg_flops": int(res["flops"]),
+                  "down_ms": round(res["down_ms"], 4)},
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layer, a.cpu_tokens)
+    del layer
+    extra = {}
+    for name in [s for s in a.also.split(",") if s]:
+        c2 = inputs.config_by_name(name)
+        r2, _ = run_config(c2, max(5, a.steps // 2), a.warmup, torch, moe, inputs)
+        d2 = "fp8" if c2.w_dtype == "fp8" else c2.act_dtype
+        extra[c2.name] = {
+            "tokens_per_s": round(c2.T / (r2["ms"] / 1e3), 1), "ms_per_step": round(r2["ms"], 4),
+            "hbm_frac": round(r2["bytes"] / (r2["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(r2["flops"] / (r2["ms"] / 1e3) / 1e12 / MFMA_PEAK_TFLOPS[d2], 4),
+            "up_kernel_ms": round(r2["up_ms"], 4), "down_kernel_ms": round(r2["down_ms"], 4),
+            "up_kernel_hbm_frac": round(r2["up_bytes"] / (r2["up_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    if extra:
+        out["also"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) forward pass of a DeepSeek-V3-style
+ * Mixture-of-Experts layer.
+ *
+ * The layer, as the DeepSeek-V3.2-Exp pages define it:
+ *   gate    ("Expert scores": formula z = x_ffn W_r, Gate.forward excerpt)
+ *           z = x W_r^T in fp32; s = sigmoid(z) or softmax(z); s' = s + bias
+ *           (selection only); keep the topk_groups best of n_groups groups
+ *           (group score = sum of its two largest s' when a bias is given,
+ *           else its largest s'); take the topk largest s'; weights are the
+ *           unbiased s of the chosen experts, divided by their sum for
+ *           sigmoid, times route_scale.
+ *   experts (routed experts and one shared MLP, SwiGLU):
+ *           FFN(v) = W2 (silu(W1 v) * (W3 v)), weights stored [out, in].
+ *   combine ("Weighted expert sum": formula y_routed = sum_i G_i E_i, the
+ *           MoE.forward excerpt and its fp32-accumulate note)
+ *           y_t = cast( sum_k w[t,k] FFN_{idx[t,k]}(x_t) + FFN_shared(x_t) ),
+ *           summed in fp32 and cast back to x's dtype.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers, row-major, owned by the caller.
+ *     The library never allocates or frees device memory; scratch space comes
+ *     from the caller's workspace (size from moe_workspace_size()).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; no call copies to the host or
+ *     synchronises.  Results are valid once the stream has reached them.
+ *   - Inputs are never written.  Outputs are fully overwritten (no need to
+ *     zero them).  Outputs must not alias inputs.
+ *   - Validation happens on the host before anything is enqueued; on an error
+ *     nothing is enqueued, outputs are untouched, and moe_last_error() gives a
+ *     readable reason (thread-local).  T == 0 is a successful no-op.
+ *   - Results are deterministic: the same inputs give bitwise-equal outputs.
+ *   - Calls that share a workspace must be ordered (same stream).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* a shape, pointer or hyper-parameter is invalid          */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid, but outside what the kernels implement           */
+  MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than moe_workspace_size()     */
+  MOE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed              */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,              /* IEEE binary32                                          */
+  MOE_BF16 = 1,             /* bfloat16 (uint16 storage)                              */
+  MOE_FP8_E4M3 = 2          /* OCP e4m3fn (uint8 storage), with fp32 block scales     */
+} moe_dtype;
+
+typedef enum moe_score {
+  MOE_SCORE_SIGMOID = 0,
+  MOE_SCORE_SOFTMAX = 1
+} moe_score;
+
+/* Shapes and hyper-parameters ("Expert scores", Gate constructor excerpt:
+ * dim, topk = activated experts, n_groups, topk_groups = limited groups,
+ * score_func, route_scale; routed and shared widths from the MoE constructor
+ * Expert(dim, moe_inter_dim) and MLP(dim, n_shared_experts * moe_inter_dim)).
+ *
+ * Supported combinations:
+ *   act_dtype = router_dtype = weight_dtype = MOE_F32, or
+ *   act_dtype = router_dtype = MOE_BF16 with weight_dtype MOE_BF16 or MOE_FP8_E4M3.
+ * Limits: 1 <= n_experts <= 512; n_experts % n_groups == 0; n_groups <= 64;
+ *   1 <= topk_groups <= n_groups; 1 <= topk <= 32 and topk <= topk_groups *
+ *   n_experts / n_groups; with a bias and n_groups > 1 each group needs >= 2
+ *   experts; dim, inter and shared_inter multiples of 64 (of 128 for fp8).   */
+typedef struct moe_params {
+  int32_t dim;           /* model width                                          */
+  int32_t n_experts;     /* E, routed experts                                    */
+  int32_t n_groups;      /* expert groups (1 = no group limit)                   */
+  int32_t topk_groups;   /* groups kept per token                                */
+  int32_t topk;          /* experts per token                                    */
+  int32_t inter;         /* inner width of every routed expert                   */
+  int32_t shared_inter;  /* inner width of the shared expert, 0 = none           */
+  int32_t score_func;    /* moe_score                                            */
+  float route_scale;     /* multiplies the routing weights                       */
+  int32_t act_dtype;     /* dtype of x and y: MOE_F32 or MOE_BF16                */
+  int32_t router_dtype;  /* dtype of W_r (applied in fp32)                       */
+  int32_t weight_dtype;  /* dtype of routed and shared expert weights            */
+} moe_params;
+
+/* Expert weights, device pointers, [out, in] row-major.
+ * fp8 scales: one fp32 per 128x128 block, [out/128, in/128] per matrix,
+ * stacked over experts for the routed ones; NULL unless weight_dtype is fp8. */
+typedef struct moe_weights {
+  const void* w_router;   /* [E, dim], router_dtype                             */
+  const float* bias;      /* [E] fp32 selection bias, or NULL for none          */
+  const void* w1;         /* [E, inter, dim]  (gate branch, goes through silu)  */
+  const void* w3;         /* [E, inter, dim]  (linear branch)                   */
+  const void* w2;         /* [E, dim, inter]  (down projection)                 */
+  const float* w1_scale;  /* [E, inter/128, dim/128]                            */
+  const float* w3_scale;  /* [E, inter/128, dim/128]                            */
+  const float* w2_scale;  /* [E, dim/128, inter/128]                            */
+  const void* ws1;        /* [shared_inter, dim]; all ws* NULL if shared_inter=0 */
+  const void* ws3;        /* [shared_inter, dim]                                */
+  const void* ws2;        /* [dim, shared_inter]                                */
+  const float* ws1_scale; /* [shared_inter/128, dim/128]                        */
+  const float* ws3_scale; /* [shared_inter/128, dim/128]                        */
+  const float* ws2_scale; /* [dim/128, shared_inter/128]                        */
+} moe_weights;
+
+/* Bytes of device workspace that moe_forward (and each step below) needs for
+ * T tokens.  Host only; enqueues nothing. */
+moe_status moe_workspace_size(const moe_params* p, int64_t T, size_t* bytes);
+
+/* Gate ("Expert scores": formula z = x_ffn W_r, Gate.forward excerpt).
+ *   x [T, dim] act_dtype; w_router [E, dim] router_dtype; bias [E] or NULL.
+ *   out topk_idx [T, topk] int32: chosen experts in descending s' order, equal
+ *       s' broken towards the lower expert id (groups likewise);
+ *   out topk_w   [T, topk] fp32: routing weights, same order.
+ *   Logits and scores are fp32.  Uses the workspace for the logits. */
+moe_status moe_gate(const moe_params* p, int64_t T, const void* x, const void* w_router,
+                    const float* bias, int32_t* topk_idx, float* topk_w,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dispatch ("Weighted expert sum", MoE.forward excerpt: bincount of the
+ * indices, then per expert the (token, slot) pairs in row-major order).
+ *   topk_idx [T, topk] int32, every id in [0, E) and distinct within a row.
+ *   out counts [E]: assignments per expert;
+ *   out offsets [E+1]: exclusive prefix sum of counts (offsets[E] = T*topk);
+ *   out sorted_token [T*topk]: token of each expert-contiguous row; inside an
+ *       expert's segment tokens ascend;
+ *   out row_of [T, topk]: row of assignment (t, k) in that order.
+ *   Bit-exact and deterministic (no order-dependent atomics). */
+moe_status moe_permute(const moe_params* p, int64_t T, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_token,
+                       int32_t* row_of, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Experts (SwiGLU; MoE constructor: Expert(dim, moe_inter_dim) per routed
+ * expert, MLP(dim, n_shared_experts * moe_inter_dim) shared).
+ *   x [T, dim]; sorted_token and offsets as produced by moe_permute (read on
+ *   the device: no host synchronisation on the per-expert counts).
+ *   out expert_out [T*topk, dim] act_dtype: row r = FFN_e(x[sorted_token[r]])
+ *       for the expert e whose segment holds r;
+ *   out shared_out [T, dim] act_dtype: FFN_shared(x_t); may be NULL (then the
+ *       shared expert is skipped) and must be NULL when shared_inter = 0.
+ *   SwiGLU pre-activations are fp32; h = silu(a1)*a3 is rounded once (bf16,
+ *   fp32, or e4m3 per 1x128 block for fp8 weights, where x is quantised the
+ *   same way); outputs are rounded to act_dtype. */
+moe_status moe_expert_ffn(const moe_params* p, int64_t T, const void* x,
+                          const int32_t* sorted_token, const int32_t* offsets,
+                          const moe_weights* w, void* expert_out, void* shared_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Combine ("Weighted expert sum": y[idx] += expert(x[idx]) * weights, fp32
+ * accumulator, shared expert added, cast back at the end).
+ *   expert_out [T*topk, dim] act_dtype; row_of [T, topk]; topk_w [T, topk] fp32;
+ *   shared_out [T, dim] or NULL.
+ *   out y [T, dim] act_dtype = cast(sum_k topk_w[t,k] * expert_out[row_of[t,k]]
+ *       + shared_out[t]); the k sum runs in slot order, in fp32. */
+moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
+                       const int32_t* row_of, const float* topk_w, const void* shared_out,
+                       void* y, void* stream);
+
+/* The whole layer: gate, dispatch, experts, combine, in one call.
+ *   x [T, dim]; out y [T, dim] act_dtype.
+ *   Optional outputs (NULL to skip): topk_idx [T, topk], topk_w [T, topk],
+ *   counts [E]. */
+moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_weights* w,
+                       void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel timing for benchmarks (not needed to use the layer).
+ * moe_profile_start(n) creates n sets of HIP events (host-side objects, no
+ * device memory).  While started, each moe_expert_ffn / moe_forward call
+ * records an event before and after its up-projection and its
+ * down-projection grouped-GEMM launches, on the call's stream, into the next
+ * set; calls beyond n are not recorded.  moe_profile_stop() waits for the
+ * recorded events, returns the number of calls recorded and the summed
+ * durations in milliseconds, and destroys the events.  Not for concurrent use
+ * from several host threads. */
+moe_status moe_profile_start(int32_t max_calls);
+moe_status moe_profile_stop(int32_t* calls, float* up_ms, float* down_ms);
+
+/* Readable name of a status; never NULL. */
+const char* moe_status_string(moe_status s);
+
+/* Reason for the last error returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t moe_abi_version(void);
+
+#define MOE_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,88 @@
+// Weighted combine of the expert outputs plus the shared expert.
+//
+// Source: "DeepSeek-V3.2-Exp · Weighted expert sum" (y_routed = sum_i G_i E_i;
+// MoE.forward excerpt: an fp32 accumulator, y[idx] += expert(x[idx]) * weight,
+// then the shared expert is added; cast back to the input dtype at the end).
+// Gather form: each token reads its topk rows of the expert outputs (found
+// through row_of), so there are no atomics and the sum order is fixed
+// (slot order, then the shared output).  Product then add, each rounded to
+// fp32, as the page's two-step update does.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {
+  __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ __forceinline__ static void store(uint16_t* p, const float (&v)[8]) {
+    uint4 u;
+    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+};
+template <> struct Vec8<float> {
+  __device__ __forceinline__ static void load(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ w,
+                                                      const T* __restrict__ shared_out,
+                                                      T* __restrict__ y, int dim, int topk) {
+  const int t = blockIdx.x;
+  const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+  if (col >= dim) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < topk; ++k) {
+    const int r = row_of[(size_t)t * topk + k];
+    const float wk = w[(size_t)t * topk + k];
+    float v[8];
+    Vec8<T>::load(out + (size_t)r * dim + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(v[i], wk));
+  }
+  if (shared_out != nullptr) {
+    float v[8];
+    Vec8<T>::load(shared_out + (size_t)t * dim + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], v[i]);
+  }
+  Vec8<T>::store(y + (size_t)t * dim + col, acc);
+}
+
+hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
+                          const void* shared_out, void* y, int ntok, int dim, int topk,
+                          bool act_f32, hipStream_t st) {
+  dim3 grid(ntok, (dim / 8 + 255) / 256);
+  if (act_f32)
+    combine_kernel<float><<<grid, 256, 0, st>>>((const float*)expert_out, row_of, topk_w,
+                                               (const float*)shared_out, (float*)y, dim, topk);
+  else
+    combine_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)expert_out, row_of, topk_w,
+                                                  (const uint16_t*)shared_out, (uint16_t*)y, dim,
+                                                  topk);
+  return hipGetLastError();
+}
+
+}  // namespace moe

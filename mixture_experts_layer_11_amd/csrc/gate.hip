@@ -1,0 +1,216 @@
+// Gate kernels: router logits on MFMA, then per-token group-limited top-k.
+//
+// Source: "DeepSeek-V3.2-Exp · Expert scores" (formula z = x_ffn W_r; the
+// router weight is held in bf16 and applied in fp32; Gate.forward excerpt).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// logits[T, E] (fp32) = x[T, dim] . W_r[E, dim]^T
+//
+// One workgroup = 4 waves computes a 16 (experts) x 16 (tokens) tile; the
+// waves split K into interleaved 64-byte chunks and the partial tiles are
+// summed in LDS in a fixed order.  A operand = router rows, B operand = token
+// rows, so each lane ends with 4 consecutive experts of one token.
+// bf16 x bf16 products are exact in fp32 and accumulate in fp32.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict__ x,
+                                                            const T* __restrict__ wr,
+                                                            float* __restrict__ logits,
+                                                            int ntok, int dim, int E) {
+  __shared__ f32x4_t part[4][kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const int tok = min(t0 + r, ntok - 1);
+  const int ex = min(e0 + r, E - 1);
+  const char* xa = reinterpret_cast<const char*>(x + (size_t)tok * dim) + 16 * g;
+  const char* wa = reinterpret_cast<const char*>(wr + (size_t)ex * dim) + 16 * g;
+  const int nchunk = dim * (int)sizeof(T) / 64;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int c = wave;
+  for (; c + 12 < nchunk; c += 16) {   // 4 chunks in flight per wave
+    uint4 a0 = ldg16(wa + 64 * c), b0 = ldg16(xa + 64 * c);
+    uint4 a1 = ldg16(wa + 64 * (c + 4)), b1 = ldg16(xa + 64 * (c + 4));
+    uint4 a2 = ldg16(wa + 64 * (c + 8)), b2 = ldg16(xa + 64 * (c + 8));
+    uint4 a3 = ldg16(wa + 64 * (c + 12)), b3 = ldg16(xa + 64 * (c + 12));
+    acc = Chunk<T>::mma(acc, a0, b0);
+    acc = Chunk<T>::mma(acc, a1, b1);
+    acc = Chunk<T>::mma(acc, a2, b2);
+    acc = Chunk<T>::mma(acc, a3, b3);
+  }
+  for (; c < nchunk; c += 4) acc = Chunk<T>::mma(acc, ldg16(wa + 64 * c), ldg16(xa + 64 * c));
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4_t s = part[0][lane];
+    s += part[1][lane];
+    s += part[2][lane];
+    s += part[3][lane];
+    const int t = t0 + r;                 // column of D = token
+    const int e = e0 + 4 * g;             // rows of D = 4 consecutive experts
+    if (t < ntok) {
+      float* out = logits + (size_t)t * E;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (e + i < E) out[e + i] = s[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection: one wave per token.
+//   s = sigmoid(z) or softmax(z); s' = s + bias (selection only)
+//   n_groups > 1: group score = top-2 sum of s' (bias given) or max s' (no
+//   bias); keep the topk_groups best groups (ties -> lower group id)
+//   topk rounds of a wave arg-max over the candidates, ordered by
+//   (s' descending, expert id ascending); the winner's unbiased s is its weight
+//   sigmoid: w /= sum(w); then w *= route_scale
+// Lane l holds experts l, l+64, ... (up to 8 per lane, E <= 512).
+// ---------------------------------------------------------------------------
+constexpr int kSelWaves = 4;
+constexpr int kMaxPerLane = 8;
+
+__global__ __launch_bounds__(256) void gate_select_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int ntok, int E,
+    int n_groups, int topk_groups, int topk, int score_softmax, float route_scale,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  __shared__ float sel[kSelWaves][512];
+  __shared__ float gscore[kSelWaves][64];
+  __shared__ int gkeep[kSelWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kSelWaves + wave;
+  const bool active = t < ntok;
+  const int tt = active ? t : ntok - 1;
+
+  float s[kMaxPerLane], sp[kMaxPerLane];
+  const float* zrow = logits + (size_t)tt * E;
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const int e = lane + 64 * j;
+    s[j] = e < E ? zrow[e] : 0.f;
+  }
+  if (score_softmax) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (lane + 64 * j < E) m = fmaxf(m, s[j]);
+    m = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      s[j] = lane + 64 * j < E ? expf(s[j] - m) : 0.f;
+      sum += s[j];
+    }
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) s[j] = s[j] / sum;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) s[j] = 1.0f / (1.0f + expf(-s[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const int e = lane + 64 * j;
+    sp[j] = (bias != nullptr && e < E) ? s[j] + bias[e] : s[j];
+  }
+
+  // candidate mask from the group stage
+  bool cand[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) cand[j] = lane + 64 * j < E;
+  if (n_groups > 1) {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (lane + 64 * j < E) sel[wave][lane + 64 * j] = sp[j];
+    __syncthreads();
+    const int gsz = E / n_groups;
+    if (lane < n_groups) {
+      const float* gp = &sel[wave][lane * gsz];
+      float gs;
+      if (bias != nullptr) {          // sum of the two largest
+        float a = -INFINITY, b = -INFINITY;
+        for (int i = 0; i < gsz; ++i) {
+          const float v = gp[i];
+          if (v > a) { b = a; a = v; } else if (v > b) { b = v; }
+        }
+        gs = a + b;
+      } else {
+        gs = -INFINITY;
+        for (int i = 0; i < gsz; ++i) gs = fmaxf(gs, gp[i]);
+      }
+      gscore[wave][lane] = gs;
+    }
+    __syncthreads();
+    if (lane < n_groups) {
+      const float mine = gscore[wave][lane];
+      int rank = 0;
+      for (int q = 0; q < n_groups; ++q) {
+        const float o = gscore[wave][q];
+        rank += (o > mine) || (o == mine && q < lane);
+      }
+      gkeep[wave][lane] = rank < topk_groups;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) cand[j] = gkeep[wave][e / gsz] != 0;
+    }
+  }
+
+  // topk rounds of wave arg-max on (s' desc, id asc)
+  float wsum = 0.f;
+  float my_w = 0.f;
+  int my_idx = 0;
+  for (int k = 0; k < topk; ++k) {
+    float bv = -INFINITY, bs = 0.f;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = lane + 64 * j;
+      if (cand[j] && (sp[j] > bv || (sp[j] == bv && e < bi))) { bv = sp[j]; bi = e; bs = s[j]; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      const float os = __shfl_xor(bs, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; bs = os; }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (lane + 64 * j == bi) cand[j] = false;
+    wsum += bs;
+    if (lane == k) { my_w = bs; my_idx = bi; }
+  }
+  if (active && lane < topk) {
+    float w = score_softmax ? my_w : my_w / wsum;
+    topk_idx[(size_t)t * topk + lane] = my_idx;
+    topk_w[(size_t)t * topk + lane] = w * route_scale;
+  }
+}
+
+hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bias, int ntok,
+                       int dim, int E, int n_groups, int topk_groups, int topk, bool softmax,
+                       float route_scale, float* logits, int32_t* topk_idx, float* topk_w,
+                       hipStream_t st) {
+  dim3 g1((ntok + 15) / 16, (E + 15) / 16);
+  if (f32)
+    router_logits_kernel<float><<<g1, 256, 0, st>>>((const float*)x, (const float*)wr, logits,
+                                                   ntok, dim, E);
+  else
+    router_logits_kernel<uint16_t><<<g1, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr,
+                                                      logits, ntok, dim, E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  gate_select_kernel<<<(ntok + kSelWaves - 1) / kSelWaves, 256, 0, st>>>(
+      logits, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0, route_scale,
+      topk_idx, topk_w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

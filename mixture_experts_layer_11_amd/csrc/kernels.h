@@ -1,0 +1,62 @@
+// Internal launchers of the MoE kernels (host side).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 32;
+constexpr int kMaxGroups = 64;
+
+// gate.hip
+hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bias, int ntok,
+                       int dim, int E, int n_groups, int topk_groups, int topk, bool softmax,
+                       float route_scale, float* logits, int32_t* topk_idx, float* topk_w,
+                       hipStream_t st);
+
+// permute.hip
+size_t permute_scratch_bytes(int ntok, int E);
+hipError_t launch_permute(const int32_t* idx, int ntok, int topk, int E, int32_t* counts,
+                          int32_t* offsets, int32_t* sorted_token, int32_t* row_of,
+                          int32_t* scratch, hipStream_t st);
+
+// ffn.hip
+enum class WKind { F32, BF16, FP8 };
+
+struct FfnProblem {
+  const void* x;               // [T, dim] act dtype (bf16 or f32)
+  const uint8_t* xq;           // fp8 path: [T, dim] e4m3 codes of x
+  const float* xs;             // fp8 path: [T, dim/128] scales
+  const int32_t* sorted_token; // [T*topk]
+  const int32_t* offsets;      // [E+1]
+  const void *w1, *w3, *w2;    // routed weights
+  const float *w1s, *w3s, *w2s;
+  const void *ws1, *ws3, *ws2; // shared weights (NULL = no shared expert)
+  const float *ws1s, *ws3s, *ws2s;
+  void* h;                     // routed h [T*topk, inter] (bf16 / f32 / e4m3)
+  float* hscale;               // fp8: routed h scales [T*topk, inter/128]
+  void* hs;                    // shared h [T, inter_s]
+  float* hsscale;              // fp8: shared h scales [T, inter_s/128]
+  void* out;                   // routed outputs [T*topk, dim] act dtype
+  void* shared_out;            // shared outputs [T, dim] act dtype (NULL = skip)
+  int32_t* sched;              // scratch, 2 * (E + 2) ints
+  int ntok, dim, E, topk, inter, inter_s;
+  bool act_f32;
+  WKind wkind;
+  hipEvent_t ev[4];            // optional timing: up start/end, down start/end (or null)
+};
+
+size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool act_f32);
+hipError_t launch_ffn(const FfnProblem& p, hipStream_t st);
+hipError_t launch_quant_x(const uint16_t* x, int ntok, int dim, uint8_t* xq, float* xs,
+                          hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
+                          const void* shared_out, void* y, int ntok, int dim, int topk,
+                          bool act_f32, hipStream_t st);
+
+}  // namespace moe

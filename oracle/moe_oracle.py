@@ -48,7 +48,7 @@ __all__ = [
     "bf16_round", "bf16_decode", "e4m3_table", "e4m3_decode", "e4m3_encode",
     "decode_weights", "quantize_act_1x128", "router_logits", "scores",
     "select_experts", "routing_weights", "gate", "permute", "swiglu",
-    "expert_ffn", "moe_forward", "moe_forward_dense", "brute_force_select",
+    "expert_ffn", "combine", "moe_forward", "moe_forward_dense", "brute_force_select",
 ]
 
 F32 = np.float32
@@ -373,6 +373,27 @@ def expert_ffn(xv: np.ndarray, w1, w3, w2, w_dtype: str, act_dtype: str,
 # ---------------------------------------------------------------------------
 
 
+def combine(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out=None) -> np.ndarray:
+    """fp32 accumulator y = 0; for each expert in ascending id, y[t] += out[t,k] * w[t,k]
+    (product then sum, each rounded to fp32); then y += shared output.
+
+    outs [T, topk, dim]: each assignment's expert output (layer-dtype values);
+    w [T, topk] fp32; idx [T, topk]; shared_out [T, dim] or None.
+    Returns the fp32 accumulator (cast it with round_to).
+    """
+    T, K, dim = outs.shape
+    y = np.zeros((T, dim), dtype=F32)
+    order = np.argsort(idx, axis=1, kind="stable")            # ascending expert id per token
+    for j in range(K):
+        k = order[:, j]
+        o = outs[np.arange(T), k].astype(F32)
+        contrib = (o * w[np.arange(T), k][:, None].astype(F32)).astype(F32)
+        y = (y + contrib).astype(F32)
+    if shared_out is not None:
+        y = (y + np.asarray(shared_out).astype(F32)).astype(F32)
+    return y
+
+
 def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_dtype,
                 router_dtype, E, n_groups, topk_groups, topk, score_func, route_scale,
                 tokens=None, route=None):
@@ -397,20 +418,19 @@ def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_d
         w, idx = (np.asarray(route[0], F32), np.asarray(route[1], np.int32))
         info = {}
     xq = quantize_act_1x128(xv)[2] if w_dtype == "fp8" else None
-    y = np.zeros(xv.shape, dtype=F32)                       # fp32 accumulator
+    outs = np.zeros(idx.shape + (xv.shape[1],))             # FFN_{idx[t,k]}(x_t)
     for e in range(E):                                      # ascending expert order
         rows, slots = np.nonzero(idx == e)
         if rows.size == 0:
             continue
         w1, w3, w2, s1, s3, s2 = expert_weights(e)
-        out = expert_ffn(xv[rows], w1, w3, w2, w_dtype, act_dtype, s1, s3, s2,
-                         None if xq is None else xq[rows])
-        contrib = (out.astype(F32) * w[rows, slots][:, None]).astype(F32)
-        y[rows] = (y[rows] + contrib).astype(F32)
+        outs[rows, slots] = expert_ffn(xv[rows], w1, w3, w2, w_dtype, act_dtype, s1, s3, s2,
+                                       None if xq is None else xq[rows])
+    sh = None
     if shared is not None:
         w1, w3, w2, s1, s3, s2 = shared
-        out = expert_ffn(xv, w1, w3, w2, w_dtype, act_dtype, s1, s3, s2, xq)
-        y = (y + out.astype(F32)).astype(F32)
+        sh = expert_ffn(xv, w1, w3, w2, w_dtype, act_dtype, s1, s3, s2, xq)
+    y = combine(outs, w, idx, sh)
     return {"y": round_to(y.astype(np.float64), act_dtype), "y32": y, "w": w, "idx": idx,
             "info": info, "tokens": tok}
 

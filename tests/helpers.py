@@ -57,3 +57,49 @@ def tiny_cfg(name="t", **kw):
                 seed=777)
     base.update(kw)
     return inputs.MoEConfig(**base)
+
+
+# ---------------------------------------------------------------------------
+# parity rule for routing (margins from the oracle's own values)
+# ---------------------------------------------------------------------------
+
+MARGIN = 1e-5
+# Weights come from fp32 logits whose summation order is free; a logit
+# difference dz moves a softmax weight by ~2*dz relative and a renormalised
+# sigmoid weight by <= dz.  The bar admits dz up to the routing margin.
+WEIGHT_RTOL = 2 * MARGIN
+
+
+def check_routing(cfg, o_w, o_idx, info, g_idx, g_w, bias):
+    """Compare GPU routing with the oracle's.
+
+    Decided tokens (oracle group and expert margins > 1e-5): the chosen sets
+    must be equal and the weights per expert within WEIGHT_RTOL relative.  Other
+    tokens: the GPU's choice must be admissible within the margin.
+    Returns the boolean mask of tokens whose sets agree.
+    """
+    T = o_idx.shape[0]
+    dec = np.minimum(info["margin_group"], info["margin_expert"]) > MARGIN
+    o_sorted = np.sort(o_idx, axis=1)
+    g_sorted = np.sort(g_idx, axis=1)
+    same = np.all(o_sorted == g_sorted, axis=1)
+    bad = np.nonzero(dec & ~same)[0]
+    assert bad.size == 0, f"decided tokens routed differently: {bad[:10]}"
+    # weights, matched by expert id
+    oo = np.argsort(o_idx, axis=1)
+    go = np.argsort(g_idx, axis=1)
+    ow = np.take_along_axis(o_w, oo, 1).astype(np.float64)
+    gw = np.take_along_axis(g_w, go, 1).astype(np.float64)
+    rel = np.abs(gw - ow) / np.maximum(np.abs(ow), 1e-30)
+    assert rel[same].max(initial=0.0) <= WEIGHT_RTOL, rel[same].max()
+    if cfg.score_func == "sigmoid":
+        np.testing.assert_allclose(g_w.astype(np.float64).sum(1), cfg.route_scale, rtol=1e-6)
+    # distinct ids in range
+    assert np.all((g_idx >= 0) & (g_idx < cfg.E))
+    assert all(len(set(r)) == cfg.topk for r in g_idx.tolist())
+    # admissibility of the rest
+    sp = info["s_sel"].astype(np.float64)
+    for t in np.nonzero(~same)[0]:
+        kth = np.sort(sp[t][o_idx[t]])[0]
+        assert np.all(sp[t][g_idx[t]] >= kth - MARGIN), t
+    return same

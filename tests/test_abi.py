@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/moe.h declares, and rejects invalid calls on the host before any HIP
+call (nothing is enqueued, so NULL device pointers are never touched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_11_amd import moe
+from mixture_experts_layer_11_amd.inputs import CONFIGS, SMALL_CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_steps():
+    d = declared_functions()
+    for name in ("moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+                 "moe_workspace_size", "moe_status_string", "moe_last_error", "moe_abi_version"):
+        assert name in d
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(moe.EXPORTS) == set(declared_functions())
+    assert L.moe_abi_version() == 1
+
+
+def test_status_strings():
+    assert moe.status_string(0) == "MOE_OK"
+    assert moe.status_string(3) == "MOE_ERR_WORKSPACE"
+    assert moe.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def _p(**kw):
+    base = moe.Params.from_config(CONFIGS[1])
+    for k, v in kw.items():
+        setattr(base, k, v)
+    return base
+
+
+def _ws_status(p, T=16):
+    n = ctypes.c_size_t()
+    return moe.lib().moe_workspace_size(ctypes.byref(p.c()), T, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_groups=3), moe.MOE_ERR_INVALID_ARG),             # 256 % 3 != 0
+    (dict(topk_groups=9), moe.MOE_ERR_INVALID_ARG),          # > n_groups
+    (dict(topk_groups=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(topk=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(topk=129), moe.MOE_ERR_INVALID_ARG),               # > topk_groups * E / n_groups
+    (dict(n_experts=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=1024, n_groups=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(dim=7100), moe.MOE_ERR_UNSUPPORTED),               # not a multiple of 64
+    (dict(inter=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="f32"), moe.MOE_ERR_UNSUPPORTED),        # mixed dtypes
+    (dict(weight_dtype="fp8", inter=2000), moe.MOE_ERR_UNSUPPORTED),
+    (dict(topk=40, topk_groups=8), moe.MOE_ERR_UNSUPPORTED),  # topk > 32
+])
+def test_invalid_params_rejected_on_host(kw, status):
+    s, _ = _ws_status(_p(**kw))
+    assert s == status
+    assert moe.lib().moe_last_error().decode() != ""
+
+
+def test_workspace_size_grows_with_T_and_is_aligned():
+    p = _p()
+    s1, n1 = _ws_status(p, 16)
+    s2, n2 = _ws_status(p, 4096)
+    assert s1 == s2 == moe.MOE_OK and 0 < n1 < n2 and n1 % 256 == 0
+    s, _ = _ws_status(p, -1)
+    assert s == moe.MOE_ERR_INVALID_ARG
+
+
+def test_null_and_workspace_errors_enqueue_nothing():
+    p = _p()
+    L = moe.lib()
+    pc = p.c()
+    i64 = 16
+    # NULL pointers -> invalid argument
+    s = L.moe_gate(ctypes.byref(pc), i64, None, None, None, None, None, None, 0, None)
+    assert s == moe.MOE_ERR_INVALID_ARG
+    # non-NULL (never dereferenced) pointers but no workspace -> workspace error
+    fake = ctypes.c_void_p(256)
+    s = L.moe_gate(ctypes.byref(pc), i64, fake, fake, None, fake, fake, None, 0, None)
+    assert s == moe.MOE_ERR_WORKSPACE
+    s = L.moe_permute(ctypes.byref(pc), i64, fake, fake, fake, fake, fake, fake, 10, None)
+    assert s == moe.MOE_ERR_WORKSPACE
+    # bias with groups of one expert is rejected (the group score needs a top-2)
+    p1 = _p(n_experts=8, n_groups=8, topk_groups=4, topk=4)
+    s = L.moe_gate(ctypes.byref(p1.c()), i64, fake, fake, fake, fake, fake, None, 0, None)
+    assert s == moe.MOE_ERR_INVALID_ARG
+    # shared_out given without a shared expert
+    p0 = _p(shared_inter=0)
+    w = moe.moe_weights(w1=256, w3=256, w2=256)
+    s = L.moe_expert_ffn(ctypes.byref(p0.c()), i64, fake, fake, fake, ctypes.byref(w), fake,
+                         fake, fake, 1 << 30, None)
+    assert s == moe.MOE_ERR_INVALID_ARG
+    # fp8 weights without scales
+    p8 = _p(weight_dtype="fp8")
+    s = L.moe_forward(ctypes.byref(p8.c()), i64, fake, ctypes.byref(w), fake, None, None, None,
+                      fake, 1 << 30, None)
+    assert s in (moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED)
+
+
+def test_zero_tokens_is_a_noop():
+    L = moe.lib()
+    for cfg in SMALL_CONFIGS:
+        p = moe.Params.from_config(cfg)
+        if p.weight_dtype == "fp8":
+            continue
+        pc = p.c()
+        w = moe.moe_weights(w_router=256, w1=256, w3=256, w2=256, ws1=256, ws3=256, ws2=256)
+        assert L.moe_forward(ctypes.byref(pc), 0, None, ctypes.byref(w), None, None, None, None,
+                             None, 0, None) == moe.MOE_OK
+        assert L.moe_gate(ctypes.byref(pc), 0, None, None, None, None, None, None, 0, None) == moe.MOE_OK
