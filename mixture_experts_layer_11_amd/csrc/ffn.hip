@@ -19,6 +19,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 
@@ -66,11 +67,20 @@ struct TileInfo {
   int mt, nt;   // tile coordinates
 };
 
-// Returns false when this workgroup has no tile.
+// Maps this workgroup to a tile; returns false when it has none.  The grid is
+// an upper bound on the tile count (the real count is only known on the
+// device), so the XCD-aware remap runs over the real count rounded up to 8:
+// every XCD then gets an equal, contiguous range of tiles (all n-tiles and
+// m-tiles of an expert next to each other, sharing its rows in that XCD's
+// L2), and the surplus workgroups exit.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ sched,
                                           const int32_t* __restrict__ offsets, int E, int ntok,
-                                          int bm, int tile, TileInfo& ti) {
-  if (tile >= sched[E + 1]) return false;
+                                          int bm, TileInfo& ti) {
+  const int total = sched[E + 1];
+  const int n8 = (total + 7) & ~7;
+  if ((int)blockIdx.x >= n8) return false;
+  const int tile = xcd_remap(blockIdx.x, n8);
+  if (tile >= total) return false;
   int lo = 0, hi = E + 1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -148,8 +158,7 @@ constexpr int kDnBN = kSkinnyWaves * 16 * kDnNT;   // output columns per workgro
 template <typename T>
 __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
   TileInfo ti;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  if (!find_tile(p.sched, p.offsets, p.E, p.ntok, 16, tile, ti)) return;
+  if (!find_tile(p.sched, p.offsets, p.E, p.ntok, 16, ti)) return;
   const bool shared = ti.g == p.E;
   const int N = shared ? p.inter_s : p.inter;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -191,9 +200,8 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
 template <typename T>
 __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   TileInfo ti;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int32_t* sched = p.sched + p.E + 2;
-  if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, tile, ti)) return;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, ti)) return;
   const bool shared = ti.g == p.E;
   const int K = shared ? p.inter_s : p.inter;
   const int N = p.dim;
@@ -227,6 +235,218 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stream tiles (prefill): up to 192 token rows x 256 weight rows per
+// workgroup of 8 waves (two per SIMD), on v_mfma_f32_32x32x16_bf16 (the
+// 32x32 shape runs at full rate on gfx950; 16x16x32 issues at half rate).
+// A tile covers a whole expert whenever it has <= 192 tokens, so each weight
+// slice is fetched from HBM once per expert.
+//   A operand = 32 weight rows per wave, loaded straight from global memory
+//     through a ring of 4 register stages (three 64-element K slices in
+//     flight); for the up projection rows 0-15 are W1 rows and rows 16-31 the
+//     same rows of W3, so a lane's result elements i and i+8 are the two
+//     branches of one h column and SwiGLU needs no data exchange.
+//   B operand = token rows, staged in LDS (double-buffered) and read by all 8
+//     waves: the slice of every n-tile of an expert is the same, so it is
+//     L2-resident.
+// Loaded HBM latency is several microseconds, so both operands run three
+// 64-element slices ahead (token slices in registers until their LDS store).
+// Memory counters retire in issue order; with equal lookahead, waiting for
+// the token slice to store never forces a newer weight slice to land early.  The K loop is instantiated for the
+// number of 32-row token sub-tiles it computes.  LDS rows are padded by 16
+// bytes so the fragment reads of a wave spread over the banks.
+// ---------------------------------------------------------------------------
+constexpr int kSBM = 192;             // token rows per tile
+constexpr int kSMT = kSBM / 32;       // 32-row token sub-tiles per tile
+constexpr int kSWaves = 8;
+constexpr int kSBN = kSWaves * 32;    // weight rows per tile
+constexpr int kSUpBN = kSBN / 2;      // h columns per up tile
+constexpr int kSBK = 64;              // K elements per step (bf16)
+constexpr int kSKs = kSBK / 16;       // MFMA k-steps per step
+constexpr int kSStride = 2 * kSBK + 16;   // LDS bytes per token row
+constexpr int kSLds = kSBM * kSStride;
+constexpr int kSTPR = 2 * kSBK / 16;                       // threads per token row
+constexpr int kSRowsPerPass = kSWaves * 64 / kSTPR;       // token rows per load pass
+constexpr int kSXLoads = kSBM / kSRowsPerPass;             // 16-byte token loads per thread
+constexpr int kSRing = 4;
+
+struct StreamSrc {
+  const char* x[kSXLoads];   // token rows (tid / kSTPR) + kSRowsPerPass*i, at byte 16*(tid % kSTPR)
+  const char* w;             // this lane's weight row, at byte 16*(lane/32)
+  int lds_st;                // LDS byte offset of this thread's token chunk
+};
+
+
+__device__ __forceinline__ f32x16_t mma32(f32x16_t c, uint4 a, uint4 b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int MT>
+__device__ __forceinline__ void stream_kloop(char (&sx)[2][kSLds], const StreamSrc& S, int nk,
+                                             f32x16_t (&acc)[kSMT]) {
+  const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
+  uint4 wr[kSRing][kSKs];        // weight slices kt .. kt+3: [slice % 4][k-step]
+  uint4 xr[kSRing][kSXLoads];    // token slices kt+1 .. kt+3 in flight: [slice % 4]
+  auto wload = [&](uint4 (&dst)[kSKs], int kt) {
+    kt = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int s = 0; s < kSKs; ++s) dst[s] = ldg16(S.w + kt * (2 * kSBK) + 32 * s);
+  };
+  auto xload = [&](uint4 (&dst)[kSXLoads], int kt) {
+    kt = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int i = 0; i < kSXLoads; ++i) dst[i] = ldg16(S.x[i] + kt * (2 * kSBK));
+  };
+  auto xstore = [&](const uint4 (&src)[kSXLoads], int buf) {
+#pragma unroll
+    for (int i = 0; i < kSXLoads; ++i)
+      *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + kSRowsPerPass * i * kSStride]) = src[i];
+  };
+  // slices 0..2 of both operands in flight, token slice 0 into LDS
+#pragma unroll
+  for (int j = 0; j < kSRing - 1; ++j) {
+    xload(xr[j], j);
+    wload(wr[j], j);
+  }
+  xstore(xr[0], 0);
+  __syncthreads();
+  // step kt (R = kt % 4, compile-time): issue token and weight slice kt+3 (in
+  // that order), compute slice kt, store token slice kt+1.  The store waits
+  // for token slice kt+1 and whatever was issued before it - slices <= kt -
+  // so slices kt+2 and kt+3 stay in flight across the barrier.
+  auto step = [&](int kt, auto R) {
+    constexpr int r = decltype(R)::value;
+    xload(xr[(r + 3) % 4], kt + 3);
+    wload(wr[(r + 3) % 4], kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    const char* sb = sx[r & 1] + fr * kSStride + 16 * fg;
+#pragma unroll
+    for (int s = 0; s < kSKs; ++s) {
+      uint4 fx[MT];
+#pragma unroll
+      for (int a = 0; a < MT; ++a)
+        fx[a] = *reinterpret_cast<const uint4*>(sb + 32 * a * kSStride + 32 * s);
+#pragma unroll
+      for (int a = 0; a < MT; ++a) acc[a] = mma32(acc[a], wr[r][s], fx[a]);
+    }
+    xstore(xr[(r + 1) % 4], (r + 1) & 1);
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  const int nmain = nk & ~3;
+  int kt = 0;
+  for (; kt < nmain; kt += 4) {
+    step(kt, I0{});
+    step(kt + 1, I1{});
+    step(kt + 2, I2{});
+    step(kt + 3, I3{});
+  }
+  if (kt < nk) step(kt, I0{});
+  if (kt + 1 < nk) step(kt + 1, I1{});
+  if (kt + 2 < nk) step(kt + 2, I2{});
+}
+
+template <bool kUp>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void stream_bf16_kernel(FfnProblem p) {
+  __shared__ __attribute__((aligned(16))) char sx[2][kSLds];
+  TileInfo ti;
+  const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, kSBM, ti)) return;
+  const bool shared = ti.g == p.E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter);
+  const int N = kUp ? (shared ? p.inter_s : p.inter) : p.dim;   // h columns / output columns
+  const int m0 = ti.mt * kSBM;
+  const int rows_left = ti.M - m0;
+
+  StreamSrc S;
+  const int lc = tid % kSTPR, lr = tid / kSTPR;
+#pragma unroll
+  for (int i = 0; i < kSXLoads; ++i) {
+    const int m = m0 + min(lr + kSRowsPerPass * i, rows_left - 1);
+    const uint16_t* row;
+    if (kUp) {
+      const int tok = shared ? m : p.sorted_token[ti.row0 + m];
+      row = static_cast<const uint16_t*>(p.x) + (size_t)tok * K;
+    } else {
+      row = shared ? static_cast<const uint16_t*>(p.hs) + (size_t)m * K
+                   : static_cast<const uint16_t*>(p.h) + (size_t)(ti.row0 + m) * K;
+    }
+    S.x[i] = reinterpret_cast<const char*>(row) + 16 * lc;
+  }
+  S.lds_st = lr * kSStride + 16 * lc;
+
+  const int fr = lane & 31, fg = lane >> 5;
+  int ncol0;                        // first output column of the wave
+  bool wave_active;
+  if (kUp) {
+    // A rows 0-15: W1 rows ncol0 + [0,16); rows 16-31: the same rows of W3
+    ncol0 = ti.nt * kSUpBN + wave * 16;
+    wave_active = ncol0 < N;
+    const int n = min(ncol0 + (fr & 15), N - 1);
+    const uint16_t* W = fr < 16 ? (shared ? static_cast<const uint16_t*>(p.ws1)
+                                          : static_cast<const uint16_t*>(p.w1) + (size_t)ti.g * N * K)
+                                : (shared ? static_cast<const uint16_t*>(p.ws3)
+                                          : static_cast<const uint16_t*>(p.w3) + (size_t)ti.g * N * K);
+    S.w = reinterpret_cast<const char*>(W + (size_t)n * K) + 16 * fg;
+  } else {
+    ncol0 = ti.nt * kSBN + wave * 32;
+    wave_active = ncol0 < N;
+    const uint16_t* W2 = shared ? static_cast<const uint16_t*>(p.ws2)
+                                : static_cast<const uint16_t*>(p.w2) + (size_t)ti.g * N * K;
+    S.w = reinterpret_cast<const char*>(W2 + (size_t)min(ncol0 + fr, N - 1) * K) + 16 * fg;
+  }
+  int m_active = (rows_left + 31) >> 5;
+  m_active = m_active > kSMT ? kSMT : m_active;
+  if (!wave_active) m_active = 1;
+
+  f32x16_t acc[kSMT];
+#pragma unroll
+  for (int a = 0; a < kSMT; ++a)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
+
+  const int nk = K / kSBK;
+  if (m_active > 4) stream_kloop<kSMT>(sx, S, nk, acc);
+  else if (m_active > 2) stream_kloop<4>(sx, S, nk, acc);
+  else if (m_active > 1) stream_kloop<2>(sx, S, nk, acc);
+  else stream_kloop<1>(sx, S, nk, acc);
+  if (!wave_active) return;
+
+  // epilogue: lane holds D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
+  // (row = weight row of the wave, col = token of the sub-tile)
+  const int ml = lane & 31, rg = 4 * (lane >> 5);
+#pragma unroll
+  for (int a = 0; a < kSMT; ++a) {
+    const int m = m0 + 32 * a + ml;
+    if (a >= m_active || m >= ti.M) continue;
+    if (kUp) {
+      uint16_t* hrow = shared ? static_cast<uint16_t*>(p.hs) + (size_t)m * N
+                              : static_cast<uint16_t*>(p.h) + (size_t)(ti.row0 + m) * N;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {       // rows 8q + rg + [0,4) of W1, 16 + same of W3
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = silu(acc[a][4 * q + i]) * acc[a][8 + 4 * q + i];
+        store4<uint16_t>(hrow + ncol0 + 8 * q + rg, v);
+      }
+    } else {
+      uint16_t* orow = shared ? static_cast<uint16_t*>(p.shared_out) + (size_t)m * N
+                              : static_cast<uint16_t*>(p.out) + (size_t)(ti.row0 + m) * N;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[a][4 * q], acc[a][4 * q + 1], acc[a][4 * q + 2], acc[a][4 * q + 3]};
+        store4<uint16_t>(orow + ncol0 + 8 * q + rg, v);
+      }
+    }
+  }
+}
+
 static inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 static inline int round8(long n) { return (int)((n + 7) / 8 * 8); }
 
@@ -246,9 +466,13 @@ size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool ac
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const bool has_shared = p.ws1 != nullptr && p.shared_out != nullptr && p.inter_s > 0;
   const long R = (long)p.ntok * p.topk;
-  const int bm = 16;
-  const int nt_up = ceil_div(p.inter, kUpBN), nt_up_s = has_shared ? ceil_div(p.inter_s, kUpBN) : 0;
-  const int nt_dn = ceil_div(p.dim, kDnBN);
+  // stream tiles once experts see enough tokens to reuse a weight slice
+  const bool wide = p.wkind == WKind::BF16 && R >= 48L * p.E && p.dim % kSBK == 0 &&
+                    p.inter % kSBK == 0 && (!has_shared || p.inter_s % kSBK == 0);
+  const int bm = wide ? kSBM : 16;
+  const int bn_up = wide ? kSUpBN : kUpBN, bn_dn = wide ? kSBN : kDnBN;
+  const int nt_up = ceil_div(p.inter, bn_up), nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
+  const int nt_dn = ceil_div(p.dim, bn_dn);
   ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.offsets, p.E, p.ntok, has_shared ? 1 : 0, bm, nt_up,
                                           nt_up_s, bm, nt_dn, p.sched);
   hipError_t err = hipGetLastError();
@@ -258,7 +482,15 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const int g_up = round8(max_tiles(R, p.E, p.ntok, has_shared, bm, nt_up, nt_up_s));
   const int g_dn = round8(max_tiles(R, p.E, p.ntok, has_shared, bm, nt_dn, nt_dn));
   auto mark = [&](int i) { if (p.ev[i]) (void)hipEventRecord(p.ev[i], st); };
-  if (p.wkind == WKind::F32) {
+  if (wide) {
+    mark(0);
+    stream_bf16_kernel<true><<<g_up, 512, 0, st>>>(q);
+    mark(1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    mark(2);
+    stream_bf16_kernel<false><<<g_dn, 512, 0, st>>>(q);
+    mark(3);
+  } else if (p.wkind == WKind::F32) {
     mark(0);
     up_skinny_kernel<float><<<g_up, 256, 0, st>>>(q);
     mark(1);

@@ -115,6 +115,14 @@ SMALL_CONFIGS = [
               score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=512,
               inter_shared=512, act_dtype="bf16", w_dtype="bf16", router_dtype="bf16",
               seed=12004),
+    MoEConfig("s5_mini_prefill_bf16", T=1000, dim=640, E=16, n_groups=4, topk_groups=2, topk=4,
+              score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=384,
+              inter_shared=256, act_dtype="bf16", w_dtype="bf16", router_dtype="bf16",
+              seed=12005),
+    MoEConfig("s6_mini_prefill_odd", T=700, dim=448, E=16, n_groups=4, topk_groups=2, topk=4,
+              score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=320,
+              inter_shared=192, act_dtype="bf16", w_dtype="bf16", router_dtype="bf16",
+              seed=12006),
 ]
 
 
