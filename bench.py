@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--also", default="c2", help="extra configs timed after the main one ('' = none)")
     return ap.parse_args()
 

@@ -162,6 +162,17 @@ moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
                        const int32_t* row_of, const float* topk_w, const void* shared_out,
                        void* y, void* stream);
 
+/* fp8 activation quantiser (the block scheme of fp8 experts: each row split
+ * into 1x128 blocks; scale = amax / 448, or 1 when the block is all zero;
+ * code = e4m3fn(v / scale) with IEEE fp32 division, round to nearest even,
+ * saturating to +-448; a zero result is code 0).  moe_expert_ffn applies it
+ * to x and to h when weight_dtype is MOE_FP8_E4M3; it is exported so the
+ * step can be used and checked on its own.
+ *   x [rows, cols] bf16, cols a multiple of 128;
+ *   out q [rows, cols] e4m3fn codes; out scales [rows, cols/128] fp32. */
+moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                         void* stream);
+
 /* The whole layer: gate, dispatch, experts, combine, in one call.
  *   x [T, dim]; out y [T, dim] act_dtype.
  *   Optional outputs (NULL to skip): topk_idx [T, topk], topk_w [T, topk],

@@ -447,6 +447,211 @@ void stream_bf16_kernel(FfnProblem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 experts (OCP e4m3fn weights with one fp32 scale per 128x128 block;
+// activations quantised per 1x128 block).  One v_mfma 16x16x128 f8f6f4 covers
+// exactly one 128-wide K block, so each block's partial product is formed in
+// a fresh accumulator and added to the fp32 result times
+// w_scale[n/128][kb] * a_scale[m][kb] ("promotion"): the scales never enter
+// the MFMA.  A operand: lane l holds row l%16, bytes 32*(l/16) .. +31 of the
+// K block; B operand likewise for the token row; result D[4*(l/16)+i][l%16].
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) int i32x8_t_;
+
+__device__ __forceinline__ f32x4_t mma_fp8(uint4 a0, uint4 a1, uint4 b0, uint4 b1) {
+  i32x8_t_ a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  i32x8_t_ b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  // formats 0/0 = e4m3 for both operands; scale exponents 127 = 2^0 (no MX scaling)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// Activation quantiser: rows of `cols` bf16 -> e4m3 codes + one fp32 scale
+// per 1x128 block.  scale = amax / 448 (1 when amax = 0); code =
+// e4m3(v / scale), IEEE division, round to nearest even, saturating.
+// 16 threads per block, 8 elements each.
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, long rows,
+                                                        int cols, uint8_t* __restrict__ q,
+                                                        float* __restrict__ sc) {
+  const long nblk = rows * (cols / 128);
+  const long blk = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  const bool ok = blk < nblk;
+  const long b = ok ? blk : nblk - 1;
+  const long r = b / (cols / 128), cb = b % (cols / 128);
+  const uint16_t* src = x + r * cols + cb * 128 + sub * 8;
+  const uint4 u = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(w[i] << 16); v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u); }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[i], scale)) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[4 + i], scale)) << (8 * i);
+  if (ok) {
+    *reinterpret_cast<uint2*>(q + r * cols + cb * 128 + sub * 8) = make_uint2(lo, hi);
+    if (sub == 0) sc[r * (cols / 128) + cb] = scale;
+  }
+}
+
+// Up projection, fp8, skinny tiles (16 tokens x 128 h columns per workgroup,
+// i.e. one 1x128 h quantisation block per token row).  Wave w owns h columns
+// [32w, 32w+32) of the tile: W1 sub-tiles j=0,1 and W3 sub-tiles j=2,3.
+__global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
+  __shared__ float wamax[kSkinnyWaves][16];
+  TileInfo ti;
+  if (!find_tile(p.sched, p.offsets, p.E, p.ntok, 16, ti)) return;
+  const bool shared = ti.g == p.E;
+  const int N = shared ? p.inter_s : p.inter;
+  const int K = p.dim, KB = K / 128;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int nbase = ti.nt * 128 + wave * 32;          // N % 128 == 0: always inside
+  const int mi = min(ti.mt * 16 + r, ti.M - 1);
+  const int tok = shared ? mi : p.sorted_token[ti.row0 + mi];
+  const char* bp = reinterpret_cast<const char*>(p.xq + (size_t)tok * K) + 32 * grp;
+  const float* bsc = p.xs + (size_t)tok * KB;
+  const uint8_t* W1 = static_cast<const uint8_t*>(shared ? p.ws1 : p.w1) + (shared ? 0 : (size_t)ti.g * N * K);
+  const uint8_t* W3 = static_cast<const uint8_t*>(shared ? p.ws3 : p.w3) + (shared ? 0 : (size_t)ti.g * N * K);
+  const float* S1 = (shared ? p.ws1s : p.w1s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nbase / 128) * KB;
+  const float* S3 = (shared ? p.ws3s : p.w3s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nbase / 128) * KB;
+  const char* ap[4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    ap[j] = reinterpret_cast<const char*>(W1 + (size_t)(nbase + 16 * j + r) * K) + 32 * grp;
+    ap[j + 2] = reinterpret_cast<const char*>(W3 + (size_t)(nbase + 16 * j + r) * K) + 32 * grp;
+  }
+  f32x4_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 a[2][4][2], b[2][2];
+  auto load = [&](int s, int kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { a[s][j][0] = ldg16(ap[j] + 128 * kb); a[s][j][1] = ldg16(ap[j] + 128 * kb + 16); }
+    b[s][0] = ldg16(bp + 128 * kb);
+    b[s][1] = ldg16(bp + 128 * kb + 16);
+  };
+  auto comp = [&](int s, int kb) {
+    const float xsc = bsc[kb];
+    const float s1 = S1[kb] * xsc, s3 = S3[kb] * xsc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t part = mma_fp8(a[s][j][0], a[s][j][1], b[s][0], b[s][1]);
+      const float sc = j < 2 ? s1 : s3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(part[i], sc, acc[j][i]);
+    }
+  };
+  load(0, 0);
+  for (int kb = 0; kb < KB; kb += 2) {
+    if (kb + 1 < KB) load(1, kb + 1);
+    comp(0, kb);
+    if (kb + 2 < KB) load(0, kb + 2);
+    if (kb + 1 < KB) comp(1, kb + 1);
+  }
+  // note: bsc is indexed per lane (token of column r); the promotion factor
+  // is per (token, K block) x per (128-row weight block, K block)
+  // h = silu(a1) * a3 for h columns nbase + 16j + 4*grp + i, token column r
+  float h[2][4];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { h[j][i] = silu(acc[j][i]) * acc[j + 2][i]; amax = fmaxf(amax, fabsf(h[j][i])); }
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  if (grp == 0) wamax[wave][r] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wamax[0][r], wamax[1][r]), fmaxf(wamax[2][r], wamax[3][r]));
+  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  const int m = ti.mt * 16 + r;
+  if (m < ti.M) {
+    const size_t row = shared ? (size_t)m : (size_t)(ti.row0 + m);
+    uint8_t* hq = static_cast<uint8_t*>(shared ? p.hs : p.h) + row * N;
+    float* hsc = (shared ? p.hsscale : p.hscale) + row * (N / 128);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk |= (uint32_t)f32_to_e4m3(__fdiv_rn(h[j][i], scale)) << (8 * i);
+      *reinterpret_cast<uint32_t*>(hq + nbase + 16 * j + 4 * grp) = pk;
+    }
+    if (wave == 0 && grp == 0) hsc[ti.nt] = scale;
+  }
+}
+
+// Down projection, fp8, skinny tiles: 16 tokens x 256 output columns.
+__global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
+  TileInfo ti;
+  const int32_t* sched = p.sched + p.E + 2;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, ti)) return;
+  const bool shared = ti.g == p.E;
+  const int K = shared ? p.inter_s : p.inter, KB = K / 128;
+  const int N = p.dim;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int nbase = ti.nt * kDnBN + wave * 16 * kDnNT;
+  if (nbase >= N) return;
+  const int mi = min(ti.mt * 16 + r, ti.M - 1);
+  const size_t hrow = shared ? (size_t)mi : (size_t)(ti.row0 + mi);
+  const char* bp = reinterpret_cast<const char*>(static_cast<const uint8_t*>(shared ? p.hs : p.h) + hrow * K) + 32 * grp;
+  const float* bsc = (shared ? p.hsscale : p.hscale) + hrow * KB;
+  const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)ti.g * N * K);
+  const float* S2 = (shared ? p.ws2s : p.w2s + (size_t)ti.g * (N / 128) * KB);
+  const char* ap[kDnNT];
+  const float* sp[kDnNT];
+#pragma unroll
+  for (int j = 0; j < kDnNT; ++j) {
+    const int n = nbase + 16 * j;
+    ap[j] = reinterpret_cast<const char*>(W2 + (size_t)(n + r) * K) + 32 * grp;
+    sp[j] = S2 + (size_t)(n / 128) * KB;
+  }
+  f32x4_t acc[kDnNT];
+#pragma unroll
+  for (int j = 0; j < kDnNT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 a[2][kDnNT][2], b[2][2];
+  auto load = [&](int s, int kb) {
+#pragma unroll
+    for (int j = 0; j < kDnNT; ++j) { a[s][j][0] = ldg16(ap[j] + 128 * kb); a[s][j][1] = ldg16(ap[j] + 128 * kb + 16); }
+    b[s][0] = ldg16(bp + 128 * kb);
+    b[s][1] = ldg16(bp + 128 * kb + 16);
+  };
+  auto comp = [&](int s, int kb) {
+    const float hsc = bsc[kb];
+#pragma unroll
+    for (int j = 0; j < kDnNT; ++j) {
+      const f32x4_t part = mma_fp8(a[s][j][0], a[s][j][1], b[s][0], b[s][1]);
+      const float sc = sp[j][kb] * hsc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(part[i], sc, acc[j][i]);
+    }
+  };
+  load(0, 0);
+  for (int kb = 0; kb < KB; kb += 2) {
+    if (kb + 1 < KB) load(1, kb + 1);
+    comp(0, kb);
+    if (kb + 2 < KB) load(0, kb + 2);
+    if (kb + 1 < KB) comp(1, kb + 1);
+  }
+  const int m = ti.mt * 16 + r;
+  if (m < ti.M) {
+    uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) + (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
+#pragma unroll
+    for (int j = 0; j < kDnNT; ++j) {
+      float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+      store4<uint16_t>(orow + nbase + 16 * j + 4 * grp, v);
+    }
+  }
+}
+
 static inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 static inline int round8(long n) { return (int)((n + 7) / 8 * 8); }
 
@@ -506,14 +711,27 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
     mark(2);
     down_skinny_kernel<uint16_t><<<g_dn, 256, 0, st>>>(q);
     mark(3);
-  } else {
-    return hipErrorNotSupported;
+  } else {   // fp8: quantise x once (the 1x128 blocks do not depend on the expert)
+    quant_fp8_kernel<<<(int)(((long)p.ntok * (p.dim / 128) * 16 + 255) / 256), 256, 0, st>>>(
+        static_cast<const uint16_t*>(p.x), p.ntok, p.dim, const_cast<uint8_t*>(p.xq),
+        const_cast<float*>(p.xs));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    mark(0);
+    up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
+    mark(1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    mark(2);
+    down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);
+    mark(3);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quant_x(const uint16_t*, int, int, uint8_t*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_quant_x(const uint16_t* x, int rows, int cols, uint8_t* xq, float* xs,
+                          hipStream_t st) {
+  quant_fp8_kernel<<<(int)(((long)rows * (cols / 128) * 16 + 255) / 256), 256, 0, st>>>(
+      x, rows, cols, xq, xs);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -189,7 +189,6 @@ moe_status do_ffn(const moe_params* p, int64_t T, const void* x, const int32_t* 
 
 moe_status check_weights(const moe_params* p, const moe_weights* w, bool need_router, bool need_shared) {
   if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
-  if (p->weight_dtype == MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts not built yet");
   if (need_router && w->w_router == nullptr) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
   if (!w->w1 || !w->w3 || !w->w2) return fail(MOE_ERR_INVALID_ARG, "w1/w3/w2 must be non-NULL");
   const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
@@ -331,6 +330,19 @@ moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
   hipError_t e = moe::launch_combine(expert_out, row_of, topk_w, shared_out, y, (int)T, p->dim,
                                      p->topk, p->act_dtype == MOE_F32, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+}
+
+moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
+                         void* stream) {
+  g_err.clear();
+  if (rows < 0 || cols < 128 || cols % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "rows >= 0 and cols a positive multiple of 128 required");
+  if (rows > ((int64_t)1 << 31) / (cols / 128)) return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+  hipError_t e = moe::launch_quant_x(static_cast<const uint16_t*>(x), (int)rows, cols, q, scales,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "quantiser launch");
 }
 
 moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_weights* w,

@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int32, []),
+        "moe_quant_fp8": (st, [_VP, i64, ctypes.c_int32, _VP, _VP, _VP]),
         "moe_profile_start": (st, [ctypes.c_int32]),
         "moe_profile_stop": (st, [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float),
                                   ctypes.POINTER(ctypes.c_float)]),
@@ -87,7 +88,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_status_string", "moe_last_error", "moe_abi_version",
-           "moe_profile_start", "moe_profile_stop")
+           "moe_profile_start", "moe_profile_stop", "moe_quant_fp8")
 
 
 def status_string(s: int) -> str:
@@ -229,6 +230,15 @@ def moe_forward(p: Params, x, w: DeviceWeights, workspace, y=None, topk_idx=None
                              _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
     return y
+
+
+def moe_quant_fp8(x, stream=None):
+    """bf16 [rows, cols] -> (e4m3fn codes uint8 [rows, cols], fp32 scales [rows, cols/128])."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    _check(lib().moe_quant_fp8(_ptr(x), rows, cols, _ptr(q), _ptr(sc), _stream(stream)))
+    return q, sc
 
 
 def moe_profile_start(max_calls: int):

@@ -20,7 +20,7 @@ DEV = "cuda"
 BF16_BAR = (2e-2, 2e-3)
 FP8_BAR = (5e-2, 5e-2)
 
-BUILT = [c for c in inputs.SMALL_CONFIGS if c.w_dtype != "fp8"]
+BUILT = list(inputs.SMALL_CONFIGS)
 ALL_SMALL = inputs.SMALL_CONFIGS
 
 
@@ -145,6 +145,27 @@ def test_expert_ffn_parity(cfg, layers):
                                  s.w1_s, s.w3_s, s.w2_s)
         mx, mean = rel_errors(moe.to_host_values(sh), sref)
         assert mx <= bar(cfg)[0] and mean <= bar(cfg)[1], (mx, mean)
+
+
+# ---------------------------------------------------------------------------
+# fp8 activation quantiser (bit-exact codes and scales)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 256), (300, 7168)])
+def test_quant_fp8_bitexact(rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32) * np.float32(3.0)
+    a[0, :128] = 0.0                                     # an all-zero block
+    if rows > 2:
+        a[1, 128 % cols:] *= np.float32(1e-30)          # tiny values: subnormal codes
+        a[2, :64] = np.float32(448.0)                   # exact saturation point
+    bits = inputs.f32_to_bf16_bits(a)
+    vals = inputs.bf16_bits_to_f32(bits)
+    q, sc = moe.moe_quant_fp8(moe.to_device(bits, "bf16"))
+    _sync()
+    oq, osc, _ = oracle.quantize_act_1x128(vals)
+    np.testing.assert_array_equal(sc.cpu().numpy(), osc)
+    np.testing.assert_array_equal(q.cpu().numpy(), oq)
 
 
 # ---------------------------------------------------------------------------
