@@ -41,7 +41,20 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--also", default="c2", help="extra configs timed after the main one ('' = none)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def up_kernel_name(cfg):
+    """Name of the up-projection kernel the library launches for cfg (the
+    library's rule: 16-token tiles unless experts average >= 48 rows and the
+    widths are multiples of 64; fp8 weights always use the fp8 kernel)."""
+    if cfg.w_dtype == "fp8":
+        return "moe::up_skinny_fp8_kernel"
+    if cfg.w_dtype == "bf16" and cfg.T * cfg.topk >= 48 * cfg.E:
+        return "moe::stream_bf16_kernel<true>"
+    return "moe::up_skinny_kernel<%s>" % ("float" if cfg.w_dtype == "f32" else "unsigned short")
 
 
 def workload_numbers(cfg, counts):
@@ -148,6 +161,14 @@ def main():
         sys.exit(2)
     import torch
 
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 5}))
+        return
     from mixture_experts_layer_11_amd import inputs, moe
     moe.lib()
     cfg = inputs.config_by_name(a.config)
@@ -157,7 +178,7 @@ def main():
     traffic = traffic_for("up_grouped_gemm", cfg.name)
     roof = {"bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "up_skinny_kernel (up-projection grouped GEMM)",
+            "kernel": up_kernel_name(cfg),
             "kernel_ms": round(res["up_ms"], 4),
             "alg_bytes_per_launch": int(res["up_bytes"])}
     layer_gbs = res["bytes"] / (res["ms"] / 1e3) / 1e9
