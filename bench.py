@@ -48,12 +48,18 @@ def parse():
 
 def up_kernel_name(cfg):
     """Name of the up-projection kernel the library launches for cfg (the
-    library's rule: 16-token tiles unless experts average >= 48 rows and the
-    widths are multiples of 64; fp8 weights always use the fp8 kernel)."""
+    library's rule, on R = T * topk routed rows: stream tiles once experts
+    average >= 128 rows (bf16) or >= 48 rows (fp8), 64-token bf16 tiles from
+    48 rows, 16-token skinny tiles below; bf16 tiles need widths that are
+    multiples of 64)."""
+    R, E = cfg.T * cfg.topk, cfg.E
     if cfg.w_dtype == "fp8":
-        return "moe::up_skinny_fp8_kernel"
-    if cfg.w_dtype == "bf16" and cfg.T * cfg.topk >= 48 * cfg.E:
-        return "moe::stream_bf16_kernel<true>"
+        return "moe::stream_fp8_kernel<true>" if R >= 48 * E else "moe::up_skinny_fp8_kernel"
+    if cfg.w_dtype == "bf16" and cfg.dim % 64 == 0 and cfg.inter % 64 == 0 and cfg.inter_shared % 64 == 0:
+        if R >= 128 * E:
+            return "moe::stream_bf16_kernel<true>"
+        if R >= 48 * E:
+            return "moe::stream_mid_bf16_kernel<true>"
     return "moe::up_skinny_kernel<%s>" % ("float" if cfg.w_dtype == "f32" else "unsigned short")
 
 

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++20",
     "-Wall", "-Wno-unused-result", "-Wno-unused-variable",
     # packed fp32 VALU ops are kept out of the device code (see the design notes)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __res
     sched[E + 2 + E + 1] = sd[g];
   }
 }
+
+typedef __attribute__((ext_vector_type(8))) int i32x8_t_;
 
 struct TileInfo {
   int g;        // group (E = shared)
@@ -249,126 +252,134 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 //   B operand = token rows, staged in LDS (double-buffered) and read by all 8
 //     waves: the slice of every n-tile of an expert is the same, so it is
 //     L2-resident.
-// Loaded HBM latency is several microseconds, so both operands run three
-// 64-element slices ahead (token slices in registers until their LDS store).
-// Memory counters retire in issue order; with equal lookahead, waiting for
-// the token slice to store never forces a newer weight slice to land early.  The K loop is instantiated for the
+// Loaded HBM latency is several microseconds, so weights run three 64-element
+// slices ahead and token slices two (in registers until their LDS store).
+// Memory counters retire in issue order; each step issues its token slice
+// before its weight slice, so waiting for a token slice to store never forces
+// a newer weight slice to land early.  The K loop is instantiated for the
 // number of 32-row token sub-tiles it computes.  LDS rows are padded by 16
 // bytes so the fragment reads of a wave spread over the banks.
 // ---------------------------------------------------------------------------
-constexpr int kSBM = 192;             // token rows per tile
-constexpr int kSMT = kSBM / 32;       // 32-row token sub-tiles per tile
-constexpr int kSWaves = 8;
-constexpr int kSBN = kSWaves * 32;    // weight rows per tile
-constexpr int kSUpBN = kSBN / 2;      // h columns per up tile
-constexpr int kSBK = 64;              // K elements per step (bf16)
-constexpr int kSKs = kSBK / 16;       // MFMA k-steps per step
-constexpr int kSStride = 2 * kSBK + 16;   // LDS bytes per token row
-constexpr int kSLds = kSBM * kSStride;
-constexpr int kSTPR = 2 * kSBK / 16;                       // threads per token row
-constexpr int kSRowsPerPass = kSWaves * 64 / kSTPR;       // token rows per load pass
-constexpr int kSXLoads = kSBM / kSRowsPerPass;             // 16-byte token loads per thread
-constexpr int kSRing = 4;
+// Tile shape of the stream kernel: BM token rows, WAVES waves of 32 weight
+// rows each, 64-element K slices.
+template <int BM_, int WAVES_, int RING_>
+struct SCfg {
+  static constexpr int BM = BM_;
+  static constexpr int WAVES = WAVES_;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int MT = BM / 32;               // 32-row token sub-tiles
+  static constexpr int BN = WAVES * 32;            // weight rows per tile
+  static constexpr int UPBN = BN / 2;              // h columns per up tile
+  static constexpr int BK = 64;                    // K elements per step
+  static constexpr int KS = BK / 16;               // MFMA k-steps per step
+  static constexpr int STRIDE = 2 * BK + 16;       // LDS bytes per token row
+  static constexpr int LDS = BM * STRIDE;
+  static constexpr int TPR = 2 * BK / 16;          // threads per token row (16 B each)
+  static constexpr int ROWS_PER_PASS = THREADS / TPR;
+  static constexpr int XLOADS = (BM + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
+  static constexpr int RING = RING_;               // weight register stages (RING-1 slices ahead)
+  static constexpr int UNROLL = RING % 2 ? 2 * RING : RING;   // multiple of RING and of 2
+};
+using SBig = SCfg<192, 8, 4>;  // whole experts of ~128-192 tokens, one workgroup per CU
+using SMid = SCfg<64, 4, 4>;   // 64-token tiles, three workgroups per CU
 
+template <class C>
 struct StreamSrc {
-  const char* x[kSXLoads];   // token rows (tid / kSTPR) + kSRowsPerPass*i, at byte 16*(tid % kSTPR)
+  const char* x[C::XLOADS];  // token rows (tid / TPR) + ROWS_PER_PASS*i, at byte 16*(tid % TPR)
   const char* w;             // this lane's weight row, at byte 16*(lane/32)
   int lds_st;                // LDS byte offset of this thread's token chunk
+  bool xact[C::XLOADS];      // row inside the tile (for BM not a multiple of the pass)
 };
-
 
 __device__ __forceinline__ f32x16_t mma32(f32x16_t c, uint4 a, uint4 b) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int MT>
-__device__ __forceinline__ void stream_kloop(char (&sx)[2][kSLds], const StreamSrc& S, int nk,
-                                             f32x16_t (&acc)[kSMT]) {
+template <class C, int MT>
+__device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const StreamSrc<C>& S, int nk,
+                                             f32x16_t (&acc)[C::MT]) {
   const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
-  uint4 wr[kSRing][kSKs];        // weight slices kt .. kt+3: [slice % 4][k-step]
-  uint4 xr[kSRing][kSXLoads];    // token slices kt+1 .. kt+3 in flight: [slice % 4]
-  auto wload = [&](uint4 (&dst)[kSKs], int kt) {
+  uint4 wr[C::RING][C::KS];   // weight slices in flight: [slice % RING][k-step]
+  uint4 xr[2][C::XLOADS];     // token slices kt+1, kt+2 in flight: [slice % 2]
+  auto wload = [&](uint4 (&dst)[C::KS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int s = 0; s < kSKs; ++s) dst[s] = ldg16(S.w + kt * (2 * kSBK) + 32 * s);
+    for (int s = 0; s < C::KS; ++s) dst[s] = ldg16(S.w + kt * (2 * C::BK) + 32 * s);
   };
-  auto xload = [&](uint4 (&dst)[kSXLoads], int kt) {
+  auto xload = [&](uint4 (&dst)[C::XLOADS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int i = 0; i < kSXLoads; ++i) dst[i] = ldg16(S.x[i] + kt * (2 * kSBK));
+    for (int i = 0; i < C::XLOADS; ++i) dst[i] = ldg16(S.x[i] + kt * (2 * C::BK));
   };
-  auto xstore = [&](const uint4 (&src)[kSXLoads], int buf) {
+  auto xstore = [&](const uint4 (&src)[C::XLOADS], int buf) {
 #pragma unroll
-    for (int i = 0; i < kSXLoads; ++i)
-      *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + kSRowsPerPass * i * kSStride]) = src[i];
+    for (int i = 0; i < C::XLOADS; ++i)
+      if (S.xact[i]) *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + C::ROWS_PER_PASS * i * C::STRIDE]) = src[i];
   };
-  // slices 0..2 of both operands in flight, token slice 0 into LDS
+  xload(xr[0], 0);
+  xload(xr[1], 1);
 #pragma unroll
-  for (int j = 0; j < kSRing - 1; ++j) {
-    xload(xr[j], j);
-    wload(wr[j], j);
-  }
+  for (int j = 0; j < C::RING - 1; ++j) wload(wr[j], j);
   xstore(xr[0], 0);
   __syncthreads();
-  // step kt (R = kt % 4, compile-time): issue token and weight slice kt+3 (in
-  // that order), compute slice kt, store token slice kt+1.  The store waits
-  // for token slice kt+1 and whatever was issued before it - slices <= kt -
-  // so slices kt+2 and kt+3 stay in flight across the barrier.
+  // step kt (R = kt % UNROLL, compile-time): issue token slice kt+2, then
+  // weight slice kt+RING-1; compute slice kt; store token slice kt+1 (issued
+  // a step earlier, before weight slice kt+RING-2), so the newer weight
+  // slices stay in flight across the barrier.
   auto step = [&](int kt, auto R) {
     constexpr int r = decltype(R)::value;
-    xload(xr[(r + 3) % 4], kt + 3);
-    wload(wr[(r + 3) % 4], kt + 3);
+    constexpr int ws = r % C::RING;
+    xload(xr[r & 1], kt + 2);
+    wload(wr[(ws + C::RING - 1) % C::RING], kt + C::RING - 1);
     __builtin_amdgcn_sched_barrier(0);
-    const char* sb = sx[r & 1] + fr * kSStride + 16 * fg;
+    const char* sb = sx[r & 1] + fr * C::STRIDE + 16 * fg;
 #pragma unroll
-    for (int s = 0; s < kSKs; ++s) {
+    for (int s = 0; s < C::KS; ++s) {
       uint4 fx[MT];
 #pragma unroll
       for (int a = 0; a < MT; ++a)
-        fx[a] = *reinterpret_cast<const uint4*>(sb + 32 * a * kSStride + 32 * s);
+        fx[a] = *reinterpret_cast<const uint4*>(sb + 32 * a * C::STRIDE + 32 * s);
 #pragma unroll
-      for (int a = 0; a < MT; ++a) acc[a] = mma32(acc[a], wr[r][s], fx[a]);
+      for (int a = 0; a < MT; ++a) acc[a] = mma32(acc[a], wr[ws][s], fx[a]);
+      // all fragment reads of this k-step ahead of its MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);   // MFMA
     }
-    xstore(xr[(r + 1) % 4], (r + 1) & 1);
+    xstore(xr[(r + 1) & 1], (r + 1) & 1);
     __syncthreads();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  const int nmain = nk & ~3;
+  auto body = [&](int kt0, auto... R) { (step(kt0 + decltype(R)::value, R), ...); };
+  auto tail = [&](int kt0, auto... R) {
+    ((kt0 + decltype(R)::value < nk ? step(kt0 + decltype(R)::value, R) : void()), ...);
+  };
+  const int nmain = nk - nk % C::UNROLL;
   int kt = 0;
-  for (; kt < nmain; kt += 4) {
-    step(kt, I0{});
-    step(kt + 1, I1{});
-    step(kt + 2, I2{});
-    step(kt + 3, I3{});
-  }
-  if (kt < nk) step(kt, I0{});
-  if (kt + 1 < nk) step(kt + 1, I1{});
-  if (kt + 2 < nk) step(kt + 2, I2{});
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    for (; kt < nmain; kt += C::UNROLL) body(kt, std::integral_constant<int, I>{}...);
+    tail(kt, std::integral_constant<int, I>{}...);
+  }(std::make_integer_sequence<int, C::UNROLL>{});
 }
 
-template <bool kUp>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void stream_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[2][kSLds];
+template <class C, bool kUp>
+__device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]) {
   TileInfo ti;
   const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
-  if (!find_tile(sched, p.offsets, p.E, p.ntok, kSBM, ti)) return;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, C::BM, ti)) return;
   const bool shared = ti.g == p.E;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter);
   const int N = kUp ? (shared ? p.inter_s : p.inter) : p.dim;   // h columns / output columns
-  const int m0 = ti.mt * kSBM;
+  const int m0 = ti.mt * C::BM;
   const int rows_left = ti.M - m0;
 
-  StreamSrc S;
-  const int lc = tid % kSTPR, lr = tid / kSTPR;
+  StreamSrc<C> S;
+  const int lc = tid % C::TPR, lr = tid / C::TPR;
 #pragma unroll
-  for (int i = 0; i < kSXLoads; ++i) {
-    const int m = m0 + min(lr + kSRowsPerPass * i, rows_left - 1);
+  for (int i = 0; i < C::XLOADS; ++i) {
+    const int tr = lr + C::ROWS_PER_PASS * i;
+    S.xact[i] = tr < C::BM;
+    const int m = m0 + min(tr, rows_left - 1);
     const uint16_t* row;
     if (kUp) {
       const int tok = shared ? m : p.sorted_token[ti.row0 + m];
@@ -379,14 +390,14 @@ void stream_bf16_kernel(FfnProblem p) {
     }
     S.x[i] = reinterpret_cast<const char*>(row) + 16 * lc;
   }
-  S.lds_st = lr * kSStride + 16 * lc;
+  S.lds_st = lr * C::STRIDE + 16 * lc;
 
   const int fr = lane & 31, fg = lane >> 5;
   int ncol0;                        // first output column of the wave
   bool wave_active;
   if (kUp) {
     // A rows 0-15: W1 rows ncol0 + [0,16); rows 16-31: the same rows of W3
-    ncol0 = ti.nt * kSUpBN + wave * 16;
+    ncol0 = ti.nt * C::UPBN + wave * 16;
     wave_active = ncol0 < N;
     const int n = min(ncol0 + (fr & 15), N - 1);
     const uint16_t* W = fr < 16 ? (shared ? static_cast<const uint16_t*>(p.ws1)
@@ -395,34 +406,39 @@ void stream_bf16_kernel(FfnProblem p) {
                                           : static_cast<const uint16_t*>(p.w3) + (size_t)ti.g * N * K);
     S.w = reinterpret_cast<const char*>(W + (size_t)n * K) + 16 * fg;
   } else {
-    ncol0 = ti.nt * kSBN + wave * 32;
+    ncol0 = ti.nt * C::BN + wave * 32;
     wave_active = ncol0 < N;
     const uint16_t* W2 = shared ? static_cast<const uint16_t*>(p.ws2)
                                 : static_cast<const uint16_t*>(p.w2) + (size_t)ti.g * N * K;
     S.w = reinterpret_cast<const char*>(W2 + (size_t)min(ncol0 + fr, N - 1) * K) + 16 * fg;
   }
   int m_active = (rows_left + 31) >> 5;
-  m_active = m_active > kSMT ? kSMT : m_active;
+  m_active = m_active > C::MT ? C::MT : m_active;
   if (!wave_active) m_active = 1;
 
-  f32x16_t acc[kSMT];
+  f32x16_t acc[C::MT];
 #pragma unroll
-  for (int a = 0; a < kSMT; ++a)
+  for (int a = 0; a < C::MT; ++a)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
 
-  const int nk = K / kSBK;
-  if (m_active > 4) stream_kloop<kSMT>(sx, S, nk, acc);
-  else if (m_active > 2) stream_kloop<4>(sx, S, nk, acc);
-  else if (m_active > 1) stream_kloop<2>(sx, S, nk, acc);
-  else stream_kloop<1>(sx, S, nk, acc);
+  const int nk = K / C::BK;
+  if constexpr (C::MT > 4) {
+    if (m_active > 4) stream_kloop<C, C::MT>(sx, S, nk, acc);
+    else if (m_active > 2) stream_kloop<C, 4>(sx, S, nk, acc);
+    else if (m_active > 1) stream_kloop<C, 2>(sx, S, nk, acc);
+    else stream_kloop<C, 1>(sx, S, nk, acc);
+  } else {
+    if (m_active > 1) stream_kloop<C, C::MT>(sx, S, nk, acc);
+    else stream_kloop<C, 1>(sx, S, nk, acc);
+  }
   if (!wave_active) return;
 
   // epilogue: lane holds D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
   // (row = weight row of the wave, col = token of the sub-tile)
   const int ml = lane & 31, rg = 4 * (lane >> 5);
 #pragma unroll
-  for (int a = 0; a < kSMT; ++a) {
+  for (int a = 0; a < C::MT; ++a) {
     const int m = m0 + 32 * a + ml;
     if (a >= m_active || m >= ti.M) continue;
     if (kUp) {
@@ -448,6 +464,267 @@ void stream_bf16_kernel(FfnProblem p) {
 }
 
 // ---------------------------------------------------------------------------
+// fp8 stream tiles (prefill): the structure of the bf16 stream tiles with
+// one 128-wide K block - one scale block - per step, on
+// v_mfma_f32_16x16x128_f8f6f4 (one MFMA per block).  Block scales are applied
+// in fp32 outside the MFMA without a separate partial: the accumulator is
+// kept in units of the current block's scale s = w_scale * a_scale (> 0), so
+// each block is T <- mfma(W, X, T * s_prev / s) and the result is T * s_last,
+// the same sum as sum_kb s_kb * (W_kb X_kb) up to one fp32 rounding per block.  A operand
+// lane l: row l%16, bytes 32*(l/16)..+31 of the block; B likewise for the
+// token row; result D[4*(l/16)+i][l%16].  Each wave owns two 16-row weight
+// sub-tiles (up projection: W1 rows and the same rows of W3; down: 32 rows
+// of W2) against 128 token rows (8 sub-tiles).  Token slices carry their
+// per-row activation scale into LDS.  The up epilogue quantises h per 1x128
+// block: the 8 waves' 16-column slices of a token row form exactly one block,
+// so the amax is reduced across waves in LDS.
+// ---------------------------------------------------------------------------
+using F8 = SCfg<128, 8, 4>;   // 128 tokens, 8 waves x 32 weight rows, ring of 4
+constexpr int kF8MT = F8::BM / 16;   // 16-row token sub-tiles
+
+struct StreamSrcF8 {
+  const char* x[F8::XLOADS];     // token rows (tid / 8) + 64*i, byte 16*(tid % 8) of the 128-byte block
+  const float* xs[F8::XLOADS];   // their activation scales, [row][K/128]
+  const char* w[2];              // this lane's rows of the two weight sub-tiles, at byte 32*(lane/16)
+  const float* ws[2];            // block scales of the two sub-tiles, [K/128]
+  int lds_st;
+};
+
+template <int MT>
+__device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (&sxs)[2][F8::BM],
+                                                 const StreamSrcF8& S, int nk,
+                                                 f32x4_t (&acc)[kF8MT][2]) {
+  constexpr int XL = F8::XLOADS, RING = F8::RING;
+  const int lane = threadIdx.x & 63, fr = lane & 15, fg = lane >> 4;
+  i32x8_t_ wr[RING][2];          // [slice % RING][sub-tile]: 32 bytes per lane
+  float wsc[RING][2];
+  uint4 xr[2][XL];
+  float xsr[2][XL];
+  float sprev[MT][2];           // scale of the accumulator's current units
+#pragma unroll
+  for (int a = 0; a < MT; ++a) sprev[a][0] = sprev[a][1] = 1.f;
+  auto wload = [&](i32x8_t_ (&dst)[2], float (&sc)[2], int kt) {
+    kt = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dst[j] = *reinterpret_cast<const i32x8_t_*>(S.w[j] + kt * 128);
+      sc[j] = S.ws[j][kt];
+    }
+  };
+  auto xload = [&](uint4 (&dst)[XL], float (&sc)[XL], int kt) {
+    kt = kt < nk ? kt : nk - 1;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      dst[i] = ldg16(S.x[i] + kt * 128);
+      sc[i] = S.xs[i][kt];       // the 8 lanes of a row load the same scale: no branch in the loop
+    }
+  };
+  auto xstore = [&](const uint4 (&src)[XL], const float (&sc)[XL], int buf) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      static_assert(F8::BM % F8::ROWS_PER_PASS == 0, "every token load pass lands inside the tile");
+      *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + F8::ROWS_PER_PASS * i * F8::STRIDE]) = src[i];
+      sxs[buf][(threadIdx.x >> 3) + F8::ROWS_PER_PASS * i] = sc[i];   // equal values from the row's 8 lanes
+    }
+  };
+  xload(xr[0], xsr[0], 0);
+  xload(xr[1], xsr[1], 1);
+#pragma unroll
+  for (int j = 0; j < RING - 1; ++j) wload(wr[j], wsc[j], j);
+  xstore(xr[0], xsr[0], 0);
+  __syncthreads();
+  auto step = [&](int kt, auto R) {
+    constexpr int r = decltype(R)::value;
+    constexpr int ws = r % RING;
+    xload(xr[r & 1], xsr[r & 1], kt + 2);
+    wload(wr[(ws + RING - 1) % RING], wsc[(ws + RING - 1) % RING], kt + RING - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // token sub-tile a+1 is read from LDS while sub-tile a is multiplied
+    const char* sb = sx[r & 1] + fr * F8::STRIDE + 32 * fg;
+    const float* sbs = sxs[r & 1] + fr;
+    i32x8_t_ bx[2];
+    float bs[2];
+    bx[0] = *reinterpret_cast<const i32x8_t_*>(sb);
+    bs[0] = sbs[0];
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      if (a + 1 < MT) {
+        bx[(a + 1) & 1] = *reinterpret_cast<const i32x8_t_*>(sb + 16 * (a + 1) * F8::STRIDE);
+        bs[(a + 1) & 1] = sbs[16 * (a + 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sc = wsc[ws][j] * bs[a & 1];
+        const float ratio = __builtin_amdgcn_rcpf(sc) * sprev[a][j];
+        sprev[a][j] = sc;
+        f32x4_t c = acc[a][j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] *= ratio;
+        acc[a][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wr[ws][j], bx[a & 1], c, 0, 0, 0, 127, 0, 127);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    xstore(xr[(r + 1) & 1], xsr[(r + 1) & 1], (r + 1) & 1);
+    __syncthreads();
+  };
+  auto body = [&](int kt0, auto... R) { (step(kt0 + decltype(R)::value, R), ...); };
+  auto tail = [&](int kt0, auto... R) {
+    ((kt0 + decltype(R)::value < nk ? step(kt0 + decltype(R)::value, R) : void()), ...);
+  };
+  const int nmain = nk - nk % F8::UNROLL;
+  int kt = 0;
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    for (; kt < nmain; kt += F8::UNROLL) body(kt, std::integral_constant<int, I>{}...);
+    tail(kt, std::integral_constant<int, I>{}...);
+  }(std::make_integer_sequence<int, F8::UNROLL>{});
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[a][j][i] *= sprev[a][j];
+}
+
+template <bool kUp>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void stream_fp8_kernel(FfnProblem p) {
+  __shared__ __attribute__((aligned(16))) char sx[2][F8::LDS];
+  __shared__ float sxs[2][F8::BM];
+  __shared__ float wamax[F8::WAVES][F8::BM];
+  TileInfo ti;
+  const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, F8::BM, ti)) return;
+  const bool shared = ti.g == p.E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter), KB = K / 128;
+  const int N = kUp ? (shared ? p.inter_s : p.inter) : p.dim;
+  const int m0 = ti.mt * F8::BM;
+  const int rows_left = ti.M - m0;
+
+  StreamSrcF8 S;
+  const int lc = tid & 7, lr = tid >> 3;
+#pragma unroll
+  for (int i = 0; i < F8::XLOADS; ++i) {
+    const int tr = lr + F8::ROWS_PER_PASS * i;
+    const int m = m0 + min(tr, rows_left - 1);
+    size_t row;
+    const uint8_t* base;
+    const float* sbase;
+    if (kUp) {
+      row = shared ? (size_t)m : (size_t)p.sorted_token[ti.row0 + m];
+      base = p.xq;
+      sbase = p.xs;
+    } else {
+      row = shared ? (size_t)m : (size_t)(ti.row0 + m);
+      base = static_cast<const uint8_t*>(shared ? p.hs : p.h);
+      sbase = shared ? p.hsscale : p.hscale;
+    }
+    S.x[i] = reinterpret_cast<const char*>(base + row * K) + 16 * lc;
+    S.xs[i] = sbase + row * KB;
+  }
+  S.lds_st = lr * F8::STRIDE + 16 * lc;
+
+  const int fr = lane & 15, fg = lane >> 4;
+  int ncol0;                      // up: first h column of the wave; down: first output column
+  if (kUp) {
+    ncol0 = ti.nt * F8::UPBN + wave * 16;          // N % 128 == 0: always inside
+    const size_t eoff = shared ? 0 : (size_t)ti.g * N * K;
+    const size_t soff = shared ? 0 : (size_t)ti.g * (N / 128) * KB;
+    const uint8_t* W1 = static_cast<const uint8_t*>(shared ? p.ws1 : p.w1) + eoff;
+    const uint8_t* W3 = static_cast<const uint8_t*>(shared ? p.ws3 : p.w3) + eoff;
+    S.w[0] = reinterpret_cast<const char*>(W1 + (size_t)(ncol0 + fr) * K) + 32 * fg;
+    S.w[1] = reinterpret_cast<const char*>(W3 + (size_t)(ncol0 + fr) * K) + 32 * fg;
+    S.ws[0] = (shared ? p.ws1s : p.w1s) + soff + (size_t)(ncol0 / 128) * KB;
+    S.ws[1] = (shared ? p.ws3s : p.w3s) + soff + (size_t)(ncol0 / 128) * KB;
+  } else {
+    ncol0 = ti.nt * F8::BN + wave * 32;
+    const int nrow = min(ncol0, N - 32);            // N % 128 == 0: a wave is all in or all out
+    const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)ti.g * N * K);
+    const float* W2s = (shared ? p.ws2s : p.w2s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nrow / 128) * KB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      S.w[j] = reinterpret_cast<const char*>(W2 + (size_t)(nrow + 16 * j + fr) * K) + 32 * fg;
+      S.ws[j] = W2s;
+    }
+  }
+  const bool wave_active = ncol0 < N;
+  int m_active = (rows_left + 15) >> 4;
+  m_active = m_active > kF8MT ? kF8MT : m_active;
+  if (!wave_active) m_active = 1;
+
+  f32x4_t acc[kF8MT][2];
+#pragma unroll
+  for (int a = 0; a < kF8MT; ++a) { acc[a][0] = f32x4_t{0.f, 0.f, 0.f, 0.f}; acc[a][1] = acc[a][0]; }
+  if (m_active > 4) stream_fp8_kloop<kF8MT>(sx, sxs, S, KB, acc);
+  else if (m_active > 2) stream_fp8_kloop<4>(sx, sxs, S, KB, acc);
+  else if (m_active > 1) stream_fp8_kloop<2>(sx, sxs, S, KB, acc);
+  else stream_fp8_kloop<1>(sx, sxs, S, KB, acc);
+
+  // result lane layout: D[n = 4*(lane/16) + i][m = lane % 16]
+  const int ml = lane & 15, nl = 4 * (lane >> 4);
+  if (kUp) {
+    // h = silu(a1) * a3 for h columns ncol0 + nl + i; one 1x128 block per token row
+#pragma unroll
+    for (int a = 0; a < kF8MT; ++a) {
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(silu(acc[a][0][i]) * acc[a][1][i]));
+      am = fmaxf(am, __shfl_xor(am, 16, kWave));
+      am = fmaxf(am, __shfl_xor(am, 32, kWave));
+      if (fg == 0) wamax[wave][16 * a + ml] = am;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < kF8MT; ++a) {
+      const int m = m0 + 16 * a + ml;
+      if (a >= m_active || m >= ti.M) continue;
+      float am = 0.f;
+#pragma unroll
+      for (int w = 0; w < F8::WAVES; ++w) am = fmaxf(am, wamax[w][16 * a + ml]);
+      const float scale = am > 0.f ? __fdiv_rn(am, 448.0f) : 1.0f;
+      const size_t row = shared ? (size_t)m : (size_t)(ti.row0 + m);
+      uint8_t* hq = static_cast<uint8_t*>(shared ? p.hs : p.h) + row * N;
+      uint32_t pk = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = silu(acc[a][0][i]) * acc[a][1][i];
+        pk |= (uint32_t)f32_to_e4m3(__fdiv_rn(v, scale)) << (8 * i);
+      }
+      *reinterpret_cast<uint32_t*>(hq + ncol0 + nl) = pk;
+      if (wave == 0 && fg == 0) (shared ? p.hsscale : p.hscale)[row * (N / 128) + ti.nt] = scale;
+    }
+  } else {
+    if (!wave_active) return;
+#pragma unroll
+    for (int a = 0; a < kF8MT; ++a) {
+      const int m = m0 + 16 * a + ml;
+      if (a >= m_active || m >= ti.M) continue;
+      uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) +
+                       (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float v[4] = {acc[a][j][0], acc[a][j][1], acc[a][j][2], acc[a][j][3]};
+        store4<uint16_t>(orow + ncol0 + 16 * j + nl, v);
+      }
+    }
+  }
+}
+
+template <bool kUp>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void stream_bf16_kernel(FfnProblem p) {
+  __shared__ __attribute__((aligned(16))) char sx[2][SBig::LDS];
+  stream_tile<SBig, kUp>(p, sx);
+}
+
+template <bool kUp>
+__global__ __launch_bounds__(256, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void stream_mid_bf16_kernel(FfnProblem p) {
+  __shared__ __attribute__((aligned(16))) char sx[2][SMid::LDS];
+  stream_tile<SMid, kUp>(p, sx);
+}
+
+// ---------------------------------------------------------------------------
 // fp8 experts (OCP e4m3fn weights with one fp32 scale per 128x128 block;
 // activations quantised per 1x128 block).  One v_mfma 16x16x128 f8f6f4 covers
 // exactly one 128-wide K block, so each block's partial product is formed in
@@ -456,7 +733,6 @@ void stream_bf16_kernel(FfnProblem p) {
 // the MFMA.  A operand: lane l holds row l%16, bytes 32*(l/16) .. +31 of the
 // K block; B operand likewise for the token row; result D[4*(l/16)+i][l%16].
 // ---------------------------------------------------------------------------
-typedef __attribute__((ext_vector_type(8))) int i32x8_t_;
 
 __device__ __forceinline__ f32x4_t mma_fp8(uint4 a0, uint4 a1, uint4 b0, uint4 b1) {
   i32x8_t_ a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
@@ -668,14 +944,31 @@ size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool ac
   return ((size_t)ntok * topk * inter + (size_t)ntok * inter_s) * esz;
 }
 
+enum class Tiles { Skinny, Mid, Big };
+
+// Tile shape for a batch: 16-token skinny tiles while experts average few
+// rows (weight streaming, no reuse to gain), 64-token tiles with several
+// workgroups per CU in between, whole-expert 192-token tiles once experts
+// average >= 128 rows.  bf16 only; widths must be multiples of 64.
+static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
+  const long R = (long)p.ntok * p.topk;
+  if (p.wkind == WKind::FP8) return R >= 48L * p.E ? Tiles::Big : Tiles::Skinny;
+  if (p.wkind != WKind::BF16) return Tiles::Skinny;
+  if (p.dim % 64 || p.inter % 64 || (has_shared && p.inter_s % 64)) return Tiles::Skinny;
+  if (R >= 128L * p.E) return Tiles::Big;
+  if (R >= 48L * p.E) return Tiles::Mid;
+  return Tiles::Skinny;
+}
+
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const bool has_shared = p.ws1 != nullptr && p.shared_out != nullptr && p.inter_s > 0;
   const long R = (long)p.ntok * p.topk;
-  // stream tiles once experts see enough tokens to reuse a weight slice
-  const bool wide = p.wkind == WKind::BF16 && R >= 48L * p.E && p.dim % kSBK == 0 &&
-                    p.inter % kSBK == 0 && (!has_shared || p.inter_s % kSBK == 0);
-  const int bm = wide ? kSBM : 16;
-  const int bn_up = wide ? kSUpBN : kUpBN, bn_dn = wide ? kSBN : kDnBN;
+  const Tiles t = pick_tiles(p, has_shared);
+  const bool f8 = p.wkind == WKind::FP8;
+  int bm = 16, bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
+  if (t == Tiles::Big && f8) bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN;
+  else if (t == Tiles::Big) bm = SBig::BM, bn_up = SBig::UPBN, bn_dn = SBig::BN;
+  else if (t == Tiles::Mid) bm = SMid::BM, bn_up = SMid::UPBN, bn_dn = SMid::BN;
   const int nt_up = ceil_div(p.inter, bn_up), nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
   const int nt_dn = ceil_div(p.dim, bn_dn);
   ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.offsets, p.E, p.ntok, has_shared ? 1 : 0, bm, nt_up,
@@ -687,43 +980,29 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const int g_up = round8(max_tiles(R, p.E, p.ntok, has_shared, bm, nt_up, nt_up_s));
   const int g_dn = round8(max_tiles(R, p.E, p.ntok, has_shared, bm, nt_dn, nt_dn));
   auto mark = [&](int i) { if (p.ev[i]) (void)hipEventRecord(p.ev[i], st); };
-  if (wide) {
-    mark(0);
-    stream_bf16_kernel<true><<<g_up, 512, 0, st>>>(q);
-    mark(1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    mark(2);
-    stream_bf16_kernel<false><<<g_dn, 512, 0, st>>>(q);
-    mark(3);
-  } else if (p.wkind == WKind::F32) {
-    mark(0);
-    up_skinny_kernel<float><<<g_up, 256, 0, st>>>(q);
-    mark(1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    mark(2);
-    down_skinny_kernel<float><<<g_dn, 256, 0, st>>>(q);
-    mark(3);
-  } else if (p.wkind == WKind::BF16) {
-    mark(0);
-    up_skinny_kernel<uint16_t><<<g_up, 256, 0, st>>>(q);
-    mark(1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    mark(2);
-    down_skinny_kernel<uint16_t><<<g_dn, 256, 0, st>>>(q);
-    mark(3);
-  } else {   // fp8: quantise x once (the 1x128 blocks do not depend on the expert)
+  if (f8) {   // quantise x once (the 1x128 blocks do not depend on the expert)
     quant_fp8_kernel<<<(int)(((long)p.ntok * (p.dim / 128) * 16 + 255) / 256), 256, 0, st>>>(
         static_cast<const uint16_t*>(p.x), p.ntok, p.dim, const_cast<uint8_t*>(p.xq),
         const_cast<float*>(p.xs));
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    mark(0);
-    up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
-    mark(1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    mark(2);
-    down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);
-    mark(3);
   }
+  mark(0);
+  if (t == Tiles::Big && f8) stream_fp8_kernel<true><<<g_up, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<true><<<g_up, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Mid) stream_mid_bf16_kernel<true><<<g_up, SMid::THREADS, 0, st>>>(q);
+  else if (p.wkind == WKind::FP8) up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
+  else if (p.wkind == WKind::BF16) up_skinny_kernel<uint16_t><<<g_up, 256, 0, st>>>(q);
+  else up_skinny_kernel<float><<<g_up, 256, 0, st>>>(q);
+  mark(1);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  mark(2);
+  if (t == Tiles::Big && f8) stream_fp8_kernel<false><<<g_dn, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<false><<<g_dn, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Mid) stream_mid_bf16_kernel<false><<<g_dn, SMid::THREADS, 0, st>>>(q);
+  else if (p.wkind == WKind::FP8) down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);
+  else if (p.wkind == WKind::BF16) down_skinny_kernel<uint16_t><<<g_dn, 256, 0, st>>>(q);
+  else down_skinny_kernel<float><<<g_dn, 256, 0, st>>>(q);
+  mark(3);
   return hipGetLastError();
 }
 

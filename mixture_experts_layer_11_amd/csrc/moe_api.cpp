@@ -1,7 +1,7 @@
 // C ABI of the MoE layer forward: host-side validation, workspace layout and
 // kernel launches.  Every device buffer is the caller's; nothing here
 // allocates, copies to the host or synchronises.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 

@@ -123,6 +123,14 @@ SMALL_CONFIGS = [
               score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=320,
               inter_shared=192, act_dtype="bf16", w_dtype="bf16", router_dtype="bf16",
               seed=12006),
+    MoEConfig("s7_mini_fp8_decode", T=40, dim=768, E=32, n_groups=4, topk_groups=2, topk=4,
+              score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=384,
+              inter_shared=256, act_dtype="bf16", w_dtype="fp8", router_dtype="bf16",
+              seed=12007),
+    MoEConfig("s8_mini_fp8_prefill_ragged", T=900, dim=384, E=8, n_groups=2, topk_groups=1,
+              topk=2, score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=640,
+              inter_shared=384, act_dtype="bf16", w_dtype="fp8", router_dtype="bf16",
+              seed=12008),
 ]
 
 
