@@ -19,6 +19,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <numeric>
 #include <type_traits>
 #include <utility>
 
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 // ---------------------------------------------------------------------------
 // Tile shape of the stream kernel: BM token rows, WAVES waves of 32 weight
 // rows each, 64-element K slices.
-template <int BM_, int WAVES_, int RING_>
+template <int BM_, int WAVES_, int RING_, int XD_ = 2>
 struct SCfg {
   static constexpr int BM = BM_;
   static constexpr int WAVES = WAVES_;
@@ -278,9 +279,10 @@ struct SCfg {
   static constexpr int ROWS_PER_PASS = THREADS / TPR;
   static constexpr int XLOADS = (BM + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
   static constexpr int RING = RING_;               // weight register stages (RING-1 slices ahead)
-  static constexpr int UNROLL = RING % 2 ? 2 * RING : RING;   // multiple of RING and of 2
+  static constexpr int XD = XD_;                   // token register stages (XD slices ahead)
+  static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), 2);   // steps with compile-time stage indices
 };
-using SBig = SCfg<192, 8, 4>;  // whole experts of ~128-192 tokens, one workgroup per CU
+using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
 using SMid = SCfg<64, 4, 4>;   // 64-token tiles, three workgroups per CU
 
 template <class C>
@@ -301,7 +303,9 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const Stream
                                              f32x16_t (&acc)[C::MT]) {
   const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
   uint4 wr[C::RING][C::KS];   // weight slices in flight: [slice % RING][k-step]
-  uint4 xr[2][C::XLOADS];     // token slices kt+1, kt+2 in flight: [slice % 2]
+  // token load passes that reach the MT*32 rows this instantiation reads
+  constexpr int XL = std::min(C::XLOADS, (32 * MT + C::ROWS_PER_PASS - 1) / C::ROWS_PER_PASS);
+  uint4 xr[C::XD][C::XLOADS]; // token slices kt+1 .. kt+XD in flight: [slice % XD]
   auto wload = [&](uint4 (&dst)[C::KS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
@@ -310,43 +314,46 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const Stream
   auto xload = [&](uint4 (&dst)[C::XLOADS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int i = 0; i < C::XLOADS; ++i) dst[i] = ldg16(S.x[i] + kt * (2 * C::BK));
+    for (int i = 0; i < XL; ++i) dst[i] = ldg16(S.x[i] + kt * (2 * C::BK));
   };
   auto xstore = [&](const uint4 (&src)[C::XLOADS], int buf) {
 #pragma unroll
-    for (int i = 0; i < C::XLOADS; ++i)
+    for (int i = 0; i < XL; ++i)
       if (S.xact[i]) *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + C::ROWS_PER_PASS * i * C::STRIDE]) = src[i];
   };
-  xload(xr[0], 0);
-  xload(xr[1], 1);
+#pragma unroll
+  for (int j = 0; j < C::XD; ++j) xload(xr[j], j);
 #pragma unroll
   for (int j = 0; j < C::RING - 1; ++j) wload(wr[j], j);
   xstore(xr[0], 0);
   __syncthreads();
-  // step kt (R = kt % UNROLL, compile-time): issue token slice kt+2, then
+  // step kt (R = kt % UNROLL, compile-time): issue token slice kt+XD, then
   // weight slice kt+RING-1; compute slice kt; store token slice kt+1 (issued
-  // a step earlier, before weight slice kt+RING-2), so the newer weight
-  // slices stay in flight across the barrier.
+  // XD-1 steps earlier), so the newer slices stay in flight across the barrier.
   auto step = [&](int kt, auto R) {
     constexpr int r = decltype(R)::value;
     constexpr int ws = r % C::RING;
-    xload(xr[r & 1], kt + 2);
+    xload(xr[r % C::XD], kt + C::XD);
     wload(wr[(ws + C::RING - 1) % C::RING], kt + C::RING - 1);
     __builtin_amdgcn_sched_barrier(0);
     const char* sb = sx[r & 1] + fr * C::STRIDE + 16 * fg;
+    // fragments of k-step s+1 are read from LDS while k-step s is multiplied
+    uint4 fx[2][MT];
+#pragma unroll
+    for (int a = 0; a < MT; ++a) fx[0][a] = *reinterpret_cast<const uint4*>(sb + 32 * a * C::STRIDE);
+    __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);     // DS read
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
-      uint4 fx[MT];
 #pragma unroll
-      for (int a = 0; a < MT; ++a)
-        fx[a] = *reinterpret_cast<const uint4*>(sb + 32 * a * C::STRIDE + 32 * s);
-#pragma unroll
-      for (int a = 0; a < MT; ++a) acc[a] = mma32(acc[a], wr[ws][s], fx[a]);
-      // all fragment reads of this k-step ahead of its MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);   // MFMA
+      for (int a = 0; a < MT; ++a) {
+        if (s + 1 < C::KS)
+          fx[(s + 1) & 1][a] = *reinterpret_cast<const uint4*>(sb + 32 * a * C::STRIDE + 32 * (s + 1));
+        acc[a] = mma32(acc[a], wr[ws][s], fx[s & 1][a]);
+        if (s + 1 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      }
     }
-    xstore(xr[(r + 1) & 1], (r + 1) & 1);
+    xstore(xr[(r + 1) % C::XD], (r + 1) & 1);
     __syncthreads();
   };
   auto body = [&](int kt0, auto... R) { (step(kt0 + decltype(R)::value, R), ...); };
@@ -412,9 +419,11 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
                                 : static_cast<const uint16_t*>(p.w2) + (size_t)ti.g * N * K;
     S.w = reinterpret_cast<const char*>(W2 + (size_t)min(ncol0 + fr, N - 1) * K) + 16 * fg;
   }
+  // every wave runs the same instantiation: the token slices are loaded by
+  // all threads of the workgroup (a wave past the last column computes on a
+  // clamped weight row and stores nothing)
   int m_active = (rows_left + 31) >> 5;
   m_active = m_active > C::MT ? C::MT : m_active;
-  if (!wave_active) m_active = 1;
 
   f32x16_t acc[C::MT];
 #pragma unroll
@@ -423,15 +432,11 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
     for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
 
   const int nk = K / C::BK;
-  if constexpr (C::MT > 4) {
-    if (m_active > 4) stream_kloop<C, C::MT>(sx, S, nk, acc);
-    else if (m_active > 2) stream_kloop<C, 4>(sx, S, nk, acc);
-    else if (m_active > 1) stream_kloop<C, 2>(sx, S, nk, acc);
-    else stream_kloop<C, 1>(sx, S, nk, acc);
-  } else {
-    if (m_active > 1) stream_kloop<C, C::MT>(sx, S, nk, acc);
-    else stream_kloop<C, 1>(sx, S, nk, acc);
-  }
+  // the K loop is instantiated for every sub-tile count, so no MFMA or token
+  // load is spent on 32-row sub-tiles past the tile's last row
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((m_active == I + 1 ? stream_kloop<C, I + 1>(sx, S, nk, acc) : void()), ...);
+  }(std::make_integer_sequence<int, C::MT>{});
   if (!wave_active) return;
 
   // epilogue: lane holds D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
@@ -494,7 +499,9 @@ template <int MT>
 __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (&sxs)[2][F8::BM],
                                                  const StreamSrcF8& S, int nk,
                                                  f32x4_t (&acc)[kF8MT][2]) {
-  constexpr int XL = F8::XLOADS, RING = F8::RING;
+  // token load passes that reach the MT*16 rows this instantiation reads
+  constexpr int XL = std::min(F8::XLOADS, (16 * MT + F8::ROWS_PER_PASS - 1) / F8::ROWS_PER_PASS);
+  constexpr int RING = F8::RING;
   const int lane = threadIdx.x & 63, fr = lane & 15, fg = lane >> 4;
   i32x8_t_ wr[RING][2];          // [slice % RING][sub-tile]: 32 bytes per lane
   float wsc[RING][2];
@@ -649,13 +656,13 @@ void stream_fp8_kernel(FfnProblem p) {
   }
   const bool wave_active = ncol0 < N;
   int m_active = (rows_left + 15) >> 4;
-  m_active = m_active > kF8MT ? kF8MT : m_active;
-  if (!wave_active) m_active = 1;
+  m_active = m_active > kF8MT ? kF8MT : m_active;   // the same for every wave (see the bf16 tiles)
 
   f32x4_t acc[kF8MT][2];
 #pragma unroll
   for (int a = 0; a < kF8MT; ++a) { acc[a][0] = f32x4_t{0.f, 0.f, 0.f, 0.f}; acc[a][1] = acc[a][0]; }
-  if (m_active > 4) stream_fp8_kloop<kF8MT>(sx, sxs, S, KB, acc);
+  if (m_active > 6) stream_fp8_kloop<kF8MT>(sx, sxs, S, KB, acc);
+  else if (m_active > 4) stream_fp8_kloop<6>(sx, sxs, S, KB, acc);
   else if (m_active > 2) stream_fp8_kloop<4>(sx, sxs, S, KB, acc);
   else if (m_active > 1) stream_fp8_kloop<2>(sx, sxs, S, KB, acc);
   else stream_fp8_kloop<1>(sx, sxs, S, KB, acc);
