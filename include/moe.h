@@ -88,9 +88,14 @@ typedef struct moe_params {
   int32_t weight_dtype;  /* dtype of routed and shared expert weights            */
 } moe_params;
 
-/* Expert weights, device pointers, [out, in] row-major.
+/* Expert weights, device pointers.  The router weight is [E, dim] row-major.
+ * The expert matrices w1, w3, w2, ws1, ws3, ws2 (logically [out, in], stacked
+ * over experts for the routed ones) are stored in the tiled layout that
+ * moe_pack_weights writes from the row-major matrix; the shapes below are the
+ * logical ones and the byte sizes are unchanged.
  * fp8 scales: one fp32 per 128x128 block, [out/128, in/128] per matrix,
- * stacked over experts for the routed ones; NULL unless weight_dtype is fp8. */
+ * row-major, stacked over experts for the routed ones; NULL unless
+ * weight_dtype is fp8. */
 typedef struct moe_weights {
   const void* w_router;   /* [E, dim], router_dtype                             */
   const float* bias;      /* [E] fp32 selection bias, or NULL for none          */
@@ -172,6 +177,19 @@ moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
  *   out q [rows, cols] e4m3fn codes; out scales [rows, cols/128] fp32. */
 moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
                          void* stream);
+
+/* Expert weight layout (a storage format of this library; the pages fix no
+ * memory layout).  Rewrites a row-major matrix of `rows` rows of `row_bytes`
+ * bytes into 16-row x 64-byte tiles: tile (i/16, j/64) of byte (i, j) is
+ * stored at ((i/16) * (row_bytes/64) + j/64) * 1024, and inside the tile the
+ * 16-byte piece (i%16, (j%64)/16) is piece number (i%16) + 16*((j%64)/16),
+ * byte j%16 within it.  Stacked expert matrices are packed in one call (rows =
+ * E * out); any element type, since the rule is on bytes.
+ *   src [rows, row_bytes] device bytes; out dst, the same size, distinct from
+ *   src.  rows must be a multiple of 16 and row_bytes a positive multiple of
+ *   64, else MOE_ERR_INVALID_ARG and nothing is enqueued. */
+moe_status moe_pack_weights(const void* src, int64_t rows, int64_t row_bytes, void* dst,
+                            void* stream);
 
 /* The whole layer: gate, dispatch, experts, combine, in one call.
  *   x [T, dim]; out y [T, dim] act_dtype.

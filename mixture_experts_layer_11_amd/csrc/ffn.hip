@@ -100,8 +100,22 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ sched,
   return true;
 }
 
+// Expert weights are stored in 16-row x 64-byte tiles (the layout
+// moe_pack_weights writes): tile (row/16, byte/64) of a matrix with row_bytes
+// bytes per row is 1 KB, made of the 16-byte pieces (row%16, (byte%64)/16) in
+// the order (row%16) + 16*((byte%64)/16) - the order in which the 64 lanes of
+// a wave hold a 16x16x32 bf16 MFMA A operand.  A wave's fragment loads are
+// then whole 128-byte lines, contiguous per tile.  Consecutive 64-byte chunks
+// of a row are 1 KB apart.
+__device__ __forceinline__ size_t wtile_off(int row, int byte, int row_bytes) {
+  return ((size_t)(row >> 4) * (row_bytes >> 6) + (byte >> 6)) * 1024 +
+         16 * ((row & 15) + 16 * ((byte >> 4) & 3)) + (byte & 15);
+}
+constexpr int kChunkStride = 1024;   // bytes between consecutive 64-byte K chunks of a tiled row
+
 // Double-buffered K loop over 64-byte chunks: U chunks per stage, NA A-operand
-// rows (16-row tiles) against one B operand.  nchunk must be a multiple of U.
+// rows (16-row tiles, tiled weights) against one B operand (a plain row).
+// nchunk must be a multiple of U.
 template <typename T, int NA, int U>
 __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* bp, int nchunk,
                                       f32x4_t (&acc)[NA]) {
@@ -110,7 +124,7 @@ __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* b
   for (int u = 0; u < U; ++u) {
     b0[u] = ldg16(bp + 64 * u);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) a0[u][j] = ldg16(ap[j] + 64 * u);
+    for (int j = 0; j < NA; ++j) a0[u][j] = ldg16(ap[j] + kChunkStride * u);
   }
   for (int c = 0; c < nchunk; c += 2 * U) {
     if (c + U < nchunk) {
@@ -118,7 +132,7 @@ __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* b
       for (int u = 0; u < U; ++u) {
         b1[u] = ldg16(bp + 64 * (c + U + u));
 #pragma unroll
-        for (int j = 0; j < NA; ++j) a1[u][j] = ldg16(ap[j] + 64 * (c + U + u));
+        for (int j = 0; j < NA; ++j) a1[u][j] = ldg16(ap[j] + kChunkStride * (c + U + u));
       }
     }
 #pragma unroll
@@ -130,7 +144,7 @@ __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* b
       for (int u = 0; u < U; ++u) {
         b0[u] = ldg16(bp + 64 * (c + 2 * U + u));
 #pragma unroll
-        for (int j = 0; j < NA; ++j) a0[u][j] = ldg16(ap[j] + 64 * (c + 2 * U + u));
+        for (int j = 0; j < NA; ++j) a0[u][j] = ldg16(ap[j] + kChunkStride * (c + 2 * U + u));
       }
     }
     if (c + U < nchunk) {
@@ -174,12 +188,13 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
   const char* bp = reinterpret_cast<const char*>(static_cast<const T*>(p.x) + (size_t)xrow * p.dim) + 16 * grp;
   const T* W1 = shared ? static_cast<const T*>(p.ws1) : static_cast<const T*>(p.w1) + (size_t)ti.g * N * p.dim;
   const T* W3 = shared ? static_cast<const T*>(p.ws3) : static_cast<const T*>(p.w3) + (size_t)ti.g * N * p.dim;
+  const int rb = p.dim * (int)sizeof(T);
   const char* ap[2 * kUpNT];
 #pragma unroll
   for (int j = 0; j < kUpNT; ++j) {
     const int n = nbase + 16 * j + r;
-    ap[j] = reinterpret_cast<const char*>(W1 + (size_t)n * p.dim) + 16 * grp;
-    ap[kUpNT + j] = reinterpret_cast<const char*>(W3 + (size_t)n * p.dim) + 16 * grp;
+    ap[j] = reinterpret_cast<const char*>(W1) + wtile_off(n, 16 * grp, rb);
+    ap[kUpNT + j] = reinterpret_cast<const char*>(W3) + wtile_off(n, 16 * grp, rb);
   }
   f32x4_t acc[2 * kUpNT];
 #pragma unroll
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   const char* ap[kDnNT];
 #pragma unroll
   for (int j = 0; j < kDnNT; ++j)
-    ap[j] = reinterpret_cast<const char*>(W2 + (size_t)(nbase + 16 * j + r) * K) + 16 * grp;
+    ap[j] = reinterpret_cast<const char*>(W2) + wtile_off(nbase + 16 * j + r, 16 * grp, K * (int)sizeof(T));
   f32x4_t acc[kDnNT];
 #pragma unroll
   for (int j = 0; j < kDnNT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -309,7 +324,8 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const Stream
   auto wload = [&](uint4 (&dst)[C::KS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) dst[s] = ldg16(S.w + kt * (2 * C::BK) + 32 * s);
+    for (int s = 0; s < C::KS; ++s)   // k-step s: bytes 32s + 16*(lane/32) of the 128-byte slice
+      dst[s] = ldg16(S.w + kt * (2 * kChunkStride) + (s >> 1) * kChunkStride + (s & 1) * 512);
   };
   auto xload = [&](uint4 (&dst)[C::XLOADS], int kt) {
     kt = kt < nk ? kt : nk - 1;
@@ -411,13 +427,13 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
                                           : static_cast<const uint16_t*>(p.w1) + (size_t)ti.g * N * K)
                                 : (shared ? static_cast<const uint16_t*>(p.ws3)
                                           : static_cast<const uint16_t*>(p.w3) + (size_t)ti.g * N * K);
-    S.w = reinterpret_cast<const char*>(W + (size_t)n * K) + 16 * fg;
+    S.w = reinterpret_cast<const char*>(W) + wtile_off(n, 16 * fg, 2 * K);
   } else {
     ncol0 = ti.nt * C::BN + wave * 32;
     wave_active = ncol0 < N;
     const uint16_t* W2 = shared ? static_cast<const uint16_t*>(p.ws2)
                                 : static_cast<const uint16_t*>(p.w2) + (size_t)ti.g * N * K;
-    S.w = reinterpret_cast<const char*>(W2 + (size_t)min(ncol0 + fr, N - 1) * K) + 16 * fg;
+    S.w = reinterpret_cast<const char*>(W2) + wtile_off(min(ncol0 + fr, N - 1), 16 * fg, 2 * K);
   }
   // every wave runs the same instantiation: the token slices are loaded by
   // all threads of the workgroup (a wave past the last column computes on a
@@ -514,7 +530,9 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      dst[j] = *reinterpret_cast<const i32x8_t_*>(S.w[j] + kt * 128);
+      const uint4 lo = ldg16(S.w[j] + kt * (2 * kChunkStride));   // bytes 32*(lane/16) + [0,16)
+      const uint4 hi = ldg16(S.w[j] + kt * (2 * kChunkStride) + 256);   // + [16,32)
+      dst[j] = i32x8_t_{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       sc[j] = S.ws[j][kt];
     }
   };
@@ -639,8 +657,8 @@ void stream_fp8_kernel(FfnProblem p) {
     const size_t soff = shared ? 0 : (size_t)ti.g * (N / 128) * KB;
     const uint8_t* W1 = static_cast<const uint8_t*>(shared ? p.ws1 : p.w1) + eoff;
     const uint8_t* W3 = static_cast<const uint8_t*>(shared ? p.ws3 : p.w3) + eoff;
-    S.w[0] = reinterpret_cast<const char*>(W1 + (size_t)(ncol0 + fr) * K) + 32 * fg;
-    S.w[1] = reinterpret_cast<const char*>(W3 + (size_t)(ncol0 + fr) * K) + 32 * fg;
+    S.w[0] = reinterpret_cast<const char*>(W1) + wtile_off(ncol0 + fr, 32 * fg, K);
+    S.w[1] = reinterpret_cast<const char*>(W3) + wtile_off(ncol0 + fr, 32 * fg, K);
     S.ws[0] = (shared ? p.ws1s : p.w1s) + soff + (size_t)(ncol0 / 128) * KB;
     S.ws[1] = (shared ? p.ws3s : p.w3s) + soff + (size_t)(ncol0 / 128) * KB;
   } else {
@@ -650,7 +668,7 @@ void stream_fp8_kernel(FfnProblem p) {
     const float* W2s = (shared ? p.ws2s : p.w2s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nrow / 128) * KB;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      S.w[j] = reinterpret_cast<const char*>(W2 + (size_t)(nrow + 16 * j + fr) * K) + 32 * fg;
+      S.w[j] = reinterpret_cast<const char*>(W2) + wtile_off(nrow + 16 * j + fr, 32 * fg, K);
       S.ws[j] = W2s;
     }
   }
@@ -809,8 +827,8 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   const char* ap[4];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    ap[j] = reinterpret_cast<const char*>(W1 + (size_t)(nbase + 16 * j + r) * K) + 32 * grp;
-    ap[j + 2] = reinterpret_cast<const char*>(W3 + (size_t)(nbase + 16 * j + r) * K) + 32 * grp;
+    ap[j] = reinterpret_cast<const char*>(W1) + wtile_off(nbase + 16 * j + r, 32 * grp, K);
+    ap[j + 2] = reinterpret_cast<const char*>(W3) + wtile_off(nbase + 16 * j + r, 32 * grp, K);
   }
   f32x4_t acc[4];
 #pragma unroll
@@ -818,7 +836,10 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   uint4 a[2][4][2], b[2][2];
   auto load = [&](int s, int kb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { a[s][j][0] = ldg16(ap[j] + 128 * kb); a[s][j][1] = ldg16(ap[j] + 128 * kb + 16); }
+    for (int j = 0; j < 4; ++j) {
+      a[s][j][0] = ldg16(ap[j] + 2 * kChunkStride * kb);
+      a[s][j][1] = ldg16(ap[j] + 2 * kChunkStride * kb + 256);
+    }
     b[s][0] = ldg16(bp + 128 * kb);
     b[s][1] = ldg16(bp + 128 * kb + 16);
   };
@@ -894,7 +915,7 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
 #pragma unroll
   for (int j = 0; j < kDnNT; ++j) {
     const int n = nbase + 16 * j;
-    ap[j] = reinterpret_cast<const char*>(W2 + (size_t)(n + r) * K) + 32 * grp;
+    ap[j] = reinterpret_cast<const char*>(W2) + wtile_off(n + r, 32 * grp, K);
     sp[j] = S2 + (size_t)(n / 128) * KB;
   }
   f32x4_t acc[kDnNT];
@@ -903,7 +924,10 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   uint4 a[2][kDnNT][2], b[2][2];
   auto load = [&](int s, int kb) {
 #pragma unroll
-    for (int j = 0; j < kDnNT; ++j) { a[s][j][0] = ldg16(ap[j] + 128 * kb); a[s][j][1] = ldg16(ap[j] + 128 * kb + 16); }
+    for (int j = 0; j < kDnNT; ++j) {
+      a[s][j][0] = ldg16(ap[j] + 2 * kChunkStride * kb);
+      a[s][j][1] = ldg16(ap[j] + 2 * kChunkStride * kb + 256);
+    }
     b[s][0] = ldg16(bp + 128 * kb);
     b[s][1] = ldg16(bp + 128 * kb + 16);
   };

@@ -54,6 +54,10 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st);
 hipError_t launch_quant_x(const uint16_t* x, int ntok, int dim, uint8_t* xq, float* xs,
                           hipStream_t st);
 
+// pack.hip
+hipError_t launch_pack_weights(const uint8_t* src, int64_t rows, int64_t row_bytes, uint8_t* dst,
+                               hipStream_t st);
+
 // combine.hip
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
                           const void* shared_out, void* y, int ntok, int dim, int topk,

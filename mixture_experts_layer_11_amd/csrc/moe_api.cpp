@@ -345,6 +345,19 @@ moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, 
   return e == hipSuccess ? MOE_OK : hip_fail(e, "quantiser launch");
 }
 
+moe_status moe_pack_weights(const void* src, int64_t rows, int64_t row_bytes, void* dst,
+                            void* stream) {
+  g_err.clear();
+  if (rows < 0 || rows % 16 != 0 || row_bytes <= 0 || row_bytes % 64 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "rows a multiple of 16 and row_bytes a positive multiple of 64 required");
+  if (rows == 0) return MOE_OK;
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+  if (src == dst) return fail(MOE_ERR_INVALID_ARG, "src and dst must be distinct buffers");
+  hipError_t e = moe::launch_pack_weights(static_cast<const uint8_t*>(src), rows, row_bytes,
+                                          static_cast<uint8_t*>(dst), (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "pack launch");
+}
+
 moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_weights* w,
                        void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
                        void* workspace, size_t workspace_bytes, void* stream) {

@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int32, []),
         "moe_quant_fp8": (st, [_VP, i64, ctypes.c_int32, _VP, _VP, _VP]),
+        "moe_pack_weights": (st, [_VP, i64, i64, _VP, _VP]),
         "moe_profile_start": (st, [ctypes.c_int32]),
         "moe_profile_stop": (st, [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float),
                                   ctypes.POINTER(ctypes.c_float)]),
@@ -88,7 +89,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_status_string", "moe_last_error", "moe_abi_version",
-           "moe_profile_start", "moe_profile_stop", "moe_quant_fp8")
+           "moe_profile_start", "moe_profile_stop", "moe_quant_fp8", "moe_pack_weights")
 
 
 def status_string(s: int) -> str:
@@ -241,6 +242,18 @@ def moe_quant_fp8(x, stream=None):
     return q, sc
 
 
+def moe_pack_weights(w, stream=None):
+    """Row-major expert matrix (device tensor whose last dim is the input width;
+    leading dims are stacked rows) -> a new tensor of the same shape and dtype
+    holding the tiled layout the expert kernels read."""
+    w = w.contiguous()
+    row_bytes = w.shape[-1] * w.element_size()
+    rows = w.numel() // w.shape[-1]
+    out = torch.empty_like(w)
+    _check(lib().moe_pack_weights(_ptr(w), rows, row_bytes, _ptr(out), _stream(stream)))
+    return out
+
+
 def moe_profile_start(max_calls: int):
     _check(lib().moe_profile_start(max_calls))
 
@@ -271,18 +284,23 @@ def to_device(a, dtype_tag: str, device="cuda") -> torch.Tensor:
 
 
 def upload_layer(layer, device="cuda") -> DeviceWeights:
-    """Copy a drawn layer's weights (storage format) to the device."""
+    """Copy a drawn layer's weights (storage format) to the device; the expert
+    matrices are rewritten into the tiled layout (moe_pack_weights)."""
     cfg = layer.cfg
     wd = cfg.w_dtype
     f32 = lambda a: None if a is None else to_device(a, "f32", device)
+
+    def mat(a):
+        t = to_device(a, wd, device)
+        packed = moe_pack_weights(t)
+        del t
+        return packed
     dw = DeviceWeights(to_device(layer.wr, cfg.router_dtype, device), f32(layer.bias),
-                       to_device(layer.w1, wd, device), to_device(layer.w3, wd, device),
-                       to_device(layer.w2, wd, device), f32(layer.w1_s), f32(layer.w3_s),
-                       f32(layer.w2_s))
+                       mat(layer.w1), mat(layer.w3), mat(layer.w2), f32(layer.w1_s),
+                       f32(layer.w3_s), f32(layer.w2_s))
     if layer.shared is not None:
         s = layer.shared
-        dw.ws1, dw.ws3, dw.ws2 = (to_device(s.w1, wd, device), to_device(s.w3, wd, device),
-                                  to_device(s.w2, wd, device))
+        dw.ws1, dw.ws3, dw.ws2 = mat(s.w1), mat(s.w3), mat(s.w2)
         dw.ws1_scale, dw.ws3_scale, dw.ws2_scale = f32(s.w1_s), f32(s.w3_s), f32(s.w2_s)
     return dw
 

@@ -114,6 +114,21 @@ def test_null_and_workspace_errors_enqueue_nothing():
     assert s in (moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED)
 
 
+@pytest.mark.parametrize("rows,row_bytes", [(15, 64), (16, 32), (16, 0), (-16, 64), (32, 100)])
+def test_pack_weights_rejects_bad_shapes(rows, row_bytes):
+    fake = ctypes.c_void_p(256)
+    other = ctypes.c_void_p(512)
+    assert moe.lib().moe_pack_weights(fake, rows, row_bytes, other, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_pack_weights_rejects_null_and_aliasing():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    assert L.moe_pack_weights(None, 16, 64, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(fake, 16, 64, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(None, 0, 64, None, None) == moe.MOE_OK     # nothing to do
+
+
 def test_zero_tokens_is_a_noop():
     L = moe.lib()
     for cfg in SMALL_CONFIGS:

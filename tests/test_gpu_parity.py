@@ -169,6 +169,29 @@ def test_quant_fp8_bitexact(rows, cols):
 
 
 # ---------------------------------------------------------------------------
+# weight layout (a storage format: checked byte for byte against its definition)
+# ---------------------------------------------------------------------------
+
+def _tiles_reference(b):
+    """[rows, row_bytes] uint8 -> the tiled byte order: tiles (row/16, byte/64)
+    in row-major tile order, inside a tile the 16-byte pieces ordered by
+    (byte%64)/16, then row%16."""
+    rows, rb = b.shape
+    return b.reshape(rows // 16, 16, rb // 64, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("rows,row_bytes", [(16, 64), (48, 128), (2048, 14336), (7168 * 2, 4096),
+                                            (96, 1792)])
+def test_pack_weights_bitexact(rows, row_bytes):
+    rng = np.random.default_rng(rows + row_bytes)
+    b = rng.integers(0, 256, (rows, row_bytes), dtype=np.uint8)
+    src = torch.from_numpy(b).to(DEV)
+    out = moe.moe_pack_weights(src)
+    _sync()
+    np.testing.assert_array_equal(out.cpu().numpy().reshape(-1), _tiles_reference(b))
+
+
+# ---------------------------------------------------------------------------
 # combine (synthetic expert outputs, oracle dispatch)
 # ---------------------------------------------------------------------------
 
