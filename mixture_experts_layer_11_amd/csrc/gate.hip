@@ -62,6 +62,104 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// bf16 router on v_mfma_f32_32x32x16_bf16: a workgroup of 4 waves computes a
+// 64-token x 64-expert tile, each wave a 32 x 32 quarter (A operand = token
+// rows, B operand = router rows, so a lane ends with one expert of 16 tokens
+// and each result row is a coalesced 128-byte store).  Fragments are loaded
+// straight from global memory through a ring of 3 register stages (64-element
+// K slices).  When the tiles alone cannot fill the GPU, K is split over
+// blockIdx.z; the split partials go to a workspace and are summed in split
+// order by router_reduce_kernel, so the result does not depend on timing.
+// ---------------------------------------------------------------------------
+constexpr int kRtTile = 64;
+constexpr int kRtMaxSplits = 16;
+
+int router_splits(int ntok, int E, int dim, int* steps_per_split) {
+  const int tiles = ((ntok + kRtTile - 1) / kRtTile) * ((E + kRtTile - 1) / kRtTile);
+  const int nk = dim / 64;
+  if (tiles <= 0 || nk <= 0) {
+    if (steps_per_split) *steps_per_split = nk;
+    return 1;
+  }
+  int S = (512 + tiles - 1) / tiles;
+  S = S < 1 ? 1 : S;
+  S = S > kRtMaxSplits ? kRtMaxSplits : S;
+  S = S > nk ? nk : S;
+  const int per = (nk + S - 1) / S;
+  if (steps_per_split) *steps_per_split = per;
+  return (nk + per - 1) / per;
+}
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          float* __restrict__ out, int ntok,
+                                                          int dim, int E, int steps_per_split,
+                                                          size_t split_stride) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRtTile + 32 * (wave & 1);
+  const int e0 = blockIdx.y * kRtTile + 32 * (wave >> 1);
+  const int nk = dim / 64;
+  const int k0 = blockIdx.z * steps_per_split;
+  const int k1 = min(nk, k0 + steps_per_split);
+  const int fr = lane & 31, fg = lane >> 5;
+  // lane: row fr of each operand, bytes 16*fg + 32*s of a 128-byte slice (k-step s)
+  const char* xa = reinterpret_cast<const char*>(x + (size_t)min(t0 + fr, ntok - 1) * dim) + 16 * fg;
+  const char* wa = reinterpret_cast<const char*>(wr + (size_t)min(e0 + fr, E - 1) * dim) + 16 * fg;
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  uint4 a[3][4], b[3][4];
+  auto load = [&](uint4 (&da)[4], uint4 (&db)[4], int kt) {
+    kt = kt < k1 ? kt : k1 - 1;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      da[s] = ldg16(xa + kt * 128 + 32 * s);
+      db[s] = ldg16(wa + kt * 128 + 32 * s);
+    }
+  };
+  auto comp = [&](const uint4 (&da)[4], const uint4 (&db)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, da[s]),
+                                                    __builtin_bit_cast(bf16x8_t, db[s]), acc, 0, 0, 0);
+  };
+  load(a[0], b[0], k0);
+  load(a[1], b[1], k0 + 1);
+  int kt = k0;
+  for (; kt + 3 <= k1; kt += 3) {
+    load(a[2], b[2], kt + 2);
+    comp(a[0], b[0]);
+    load(a[0], b[0], kt + 3);
+    comp(a[1], b[1]);
+    load(a[1], b[1], kt + 4);
+    comp(a[2], b[2]);
+  }
+  if (kt < k1) comp(a[0], b[0]);
+  if (kt + 1 < k1) comp(a[1], b[1]);
+
+  // D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane%32]: token row, expert column
+  const int e = e0 + fr;
+  if (e >= E) return;
+  float* o = out + (size_t)blockIdx.z * split_stride;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = t0 + 8 * (i / 4) + 4 * fg + (i % 4);
+    if (t < ntok) o[(size_t)t * E + e] = acc[i];
+  }
+}
+
+// logits[i] = sum over splits s = 0, 1, ... of part[s][i], in that order
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, int S,
+                                                            size_t n, float* __restrict__ logits) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[(size_t)s * n + i];
+    logits[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Selection: one wave per token.
 //   s = sigmoid(z) or softmax(z); s' = s + bias (selection only)
 //   n_groups > 1: group score = top-2 sum of s' (bias given) or max s' (no
@@ -196,15 +294,24 @@ __global__ __launch_bounds__(256) void gate_select_kernel(
 
 hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bias, int ntok,
                        int dim, int E, int n_groups, int topk_groups, int topk, bool softmax,
-                       float route_scale, float* logits, int32_t* topk_idx, float* topk_w,
-                       hipStream_t st) {
-  dim3 g1((ntok + 15) / 16, (E + 15) / 16);
-  if (f32)
+                       float route_scale, float* logits, float* rpart, int32_t* topk_idx,
+                       float* topk_w, hipStream_t st) {
+  if (f32) {
+    dim3 g1((ntok + 15) / 16, (E + 15) / 16);
     router_logits_kernel<float><<<g1, 256, 0, st>>>((const float*)x, (const float*)wr, logits,
                                                    ntok, dim, E);
-  else
-    router_logits_kernel<uint16_t><<<g1, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr,
-                                                      logits, ntok, dim, E);
+  } else {
+    int per = 0;
+    const int S = router_splits(ntok, E, dim, &per);
+    const size_t n = (size_t)ntok * E;
+    dim3 g((ntok + kRtTile - 1) / kRtTile, (E + kRtTile - 1) / kRtTile, S);
+    router_mfma_kernel<<<g, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr,
+                                          S > 1 ? rpart : logits, ntok, dim, E, per, n);
+    if (S > 1) {
+      const size_t blocks = (n + 255) / 256;
+      router_reduce_kernel<<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(rpart, S, n, logits);
+    }
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   gate_select_kernel<<<(ntok + kSelWaves - 1) / kSelWaves, 256, 0, st>>>(

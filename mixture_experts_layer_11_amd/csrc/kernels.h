@@ -12,10 +12,13 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxGroups = 64;
 
 // gate.hip
+// K splits of the bf16 router for these sizes (1 = none); rpart must then hold
+// splits * ntok * E floats.
+int router_splits(int ntok, int E, int dim, int* steps_per_split);
 hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bias, int ntok,
                        int dim, int E, int n_groups, int topk_groups, int topk, bool softmax,
-                       float route_scale, float* logits, int32_t* topk_idx, float* topk_w,
-                       hipStream_t st);
+                       float route_scale, float* logits, float* rpart, int32_t* topk_idx,
+                       float* topk_w, hipStream_t st);
 
 // permute.hip
 size_t permute_scratch_bytes(int ntok, int E);

@@ -48,7 +48,7 @@ size_t align_up(size_t n) { return (n + 255) & ~size_t(255); }
 
 // Workspace carve-up (offsets in bytes, each 256-byte aligned).
 struct Layout {
-  size_t logits, topk_idx, topk_w, counts, offsets, sorted_token, row_of, perm, sched;
+  size_t logits, rpart, topk_idx, topk_w, counts, offsets, sorted_token, row_of, perm, sched;
   size_t h, hscale, hs, hsscale, xq, xs, out, shared_out, total;
 };
 
@@ -68,6 +68,8 @@ Layout layout(const moe_params* p, int64_t T) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align_up(bytes); return at; };
   L.logits = take((size_t)T * E * 4);
+  const int splits = p->act_dtype == MOE_F32 ? 1 : moe::router_splits((int)T, (int)E, p->dim, nullptr);
+  L.rpart = take(splits > 1 ? (size_t)splits * T * E * 4 : 0);   // K-split router partials
   L.topk_idx = take(R * 4);
   L.topk_w = take(R * 4);
   L.counts = take(E * 4);
@@ -142,7 +144,7 @@ moe_status do_gate(const moe_params* p, int64_t T, const void* x, const void* wr
   hipError_t e = moe::launch_gate(x, wr, p->act_dtype == MOE_F32, bias, (int)T, p->dim,
                                   p->n_experts, p->n_groups, p->topk_groups, p->topk,
                                   p->score_func == MOE_SCORE_SOFTMAX, p->route_scale,
-                                  at<float>(ws, L.logits), idx, w, st);
+                                  at<float>(ws, L.logits), at<float>(ws, L.rpart), idx, w, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gate launch");
 }
 

@@ -7,15 +7,19 @@
 //            the totals do not depend on their order)
 //   scan   : per expert, exclusive prefix over blocks; then exclusive prefix
 //            over experts -> counts, offsets, and each block's base row
-//   scatter: per block, one thread per expert walks the block's tokens in
-//            ascending order and hands out consecutive rows
+//   scatter: per block, a bit mask per expert of the block's tokens that
+//            chose it (LDS atomic OR); the row of assignment (t, k) to expert
+//            e is the block base of e plus the number of earlier tokens of the
+//            block in e's mask (a token picks an expert at most once, so this
+//            is its rank in row-major order)
 // No step depends on the order of atomics, so the result is bit-exact.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kPermBlock = 64;   // tokens per block
+constexpr int kPermBlock = 256;   // tokens per block
+constexpr int kPermWords = kPermBlock / 64;   // 64-bit mask words per expert
 
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx,
                                                             int ntok, int topk, int E,
@@ -43,10 +47,15 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_count[(size_t)b * E + e];
-      blk_count[(size_t)b * E + e] = total;     // exclusive prefix over blocks
-      total += c;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {      // 8 independent loads in flight
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = b0 + j < nblk ? blk_count[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b0 + j < nblk) blk_count[(size_t)(b0 + j) * E + e] = total;   // exclusive prefix over blocks
+        total += c[j];
+      }
     }
   }
   buf[e] = e < E ? total : 0;
@@ -71,23 +80,25 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ idx, int ntok, int topk, int E,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ sorted_token,
     int32_t* __restrict__ row_of) {
-  __shared__ int32_t sidx[kPermBlock * kMaxTopk];
-  const int t0 = blockIdx.x * kPermBlock;
-  const int nt = min(kPermBlock, ntok - t0);
-  const int32_t* p = idx + (size_t)t0 * topk;
-  for (int i = threadIdx.x; i < nt * topk; i += blockDim.x) sidx[i] = p[i];
+  __shared__ unsigned long long mask[kMaxExperts][kPermWords];
+  for (int i = threadIdx.x; i < E * kPermWords; i += blockDim.x) (&mask[0][0])[i] = 0ull;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int pos = blk_base[(size_t)blockIdx.x * E + e];
-    for (int t = 0; t < nt; ++t) {
-      for (int k = 0; k < topk; ++k) {
-        if (sidx[t * topk + k] == e) {
-          sorted_token[pos] = t0 + t;
-          row_of[(size_t)(t0 + t) * topk + k] = pos;
-          ++pos;
-        }
-      }
-    }
+  const int t0 = blockIdx.x * kPermBlock;
+  const int n = min(kPermBlock, ntok - t0) * topk;
+  const int32_t* p = idx + (size_t)t0 * topk;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = p[i], t = i / topk;
+    if (e >= 0 && e < E) atomicOr(&mask[e][t >> 6], 1ull << (t & 63));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = p[i], t = i / topk, k = i - t * topk;
+    if (e < 0 || e >= E) continue;
+    int rank = __popcll(mask[e][t >> 6] & ((1ull << (t & 63)) - 1ull));
+    for (int w = 0; w < (t >> 6); ++w) rank += __popcll(mask[e][w]);
+    const int pos = blk_base[(size_t)blockIdx.x * E + e] + rank;
+    sorted_token[pos] = t0 + t;
+    row_of[(size_t)(t0 + t) * topk + k] = pos;
   }
 }
 
