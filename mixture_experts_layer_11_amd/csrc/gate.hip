@@ -63,15 +63,19 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict_
 
 // ---------------------------------------------------------------------------
 // bf16 router on v_mfma_f32_32x32x16_bf16: a workgroup of 4 waves computes a
-// 64-token x 64-expert tile, each wave a 32 x 32 quarter (A operand = token
-// rows, B operand = router rows, so a lane ends with one expert of 16 tokens
-// and each result row is a coalesced 128-byte store).  Fragments are loaded
-// straight from global memory through a ring of 3 register stages (64-element
-// K slices).  When the tiles alone cannot fill the GPU, K is split over
-// blockIdx.z; the split partials go to a workspace and are summed in split
-// order by router_reduce_kernel, so the result does not depend on timing.
+// 128-token x 128-expert tile; wave w owns the 64 x 64 quarter (tokens
+// 64*(w&1), experts 64*(w>>1)) as 2 x 2 MFMA tiles (A operand = token rows,
+// B operand = router rows, so a lane ends with one expert of 16 tokens per
+// tile and each result row is a coalesced 128-byte store).  Both operand
+// tiles go through LDS in 64-element K slices, double-buffered, each slice
+// loaded into registers two steps ahead.  When the tiles alone cannot fill
+// the GPU, K is split over blockIdx.z; the split partials go to a workspace
+// and are summed in split order by router_reduce_kernel, so the result does
+// not depend on timing.
 // ---------------------------------------------------------------------------
-constexpr int kRtTile = 64;
+constexpr int kRtTile = 128;              // tokens and experts per workgroup
+constexpr int kRtStride = 144;            // LDS bytes per 128-byte row slice (padded)
+constexpr int kRtPass = 4;                // 16-byte loads per operand per thread per slice
 constexpr int kRtMaxSplits = 16;
 
 int router_splits(int ntok, int E, int dim, int* steps_per_split) {
@@ -90,61 +94,105 @@ int router_splits(int ntok, int E, int dim, int* steps_per_split) {
   return (nk + per - 1) / per;
 }
 
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ wr,
-                                                          float* __restrict__ out, int ntok,
-                                                          int dim, int E, int steps_per_split,
-                                                          size_t split_stride) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kRtTile + 32 * (wave & 1);
-  const int e0 = blockIdx.y * kRtTile + 32 * (wave >> 1);
+__global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wr,
+                                                             float* __restrict__ out, int ntok,
+                                                             int dim, int E, int steps_per_split,
+                                                             size_t split_stride) {
+  __shared__ __attribute__((aligned(16))) char sx[2][kRtTile * kRtStride];
+  __shared__ __attribute__((aligned(16))) char sw[2][kRtTile * kRtStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tb = blockIdx.x * kRtTile, eb = blockIdx.y * kRtTile;
   const int nk = dim / 64;
   const int k0 = blockIdx.z * steps_per_split;
   const int k1 = min(nk, k0 + steps_per_split);
-  const int fr = lane & 31, fg = lane >> 5;
-  // lane: row fr of each operand, bytes 16*fg + 32*s of a 128-byte slice (k-step s)
-  const char* xa = reinterpret_cast<const char*>(x + (size_t)min(t0 + fr, ntok - 1) * dim) + 16 * fg;
-  const char* wa = reinterpret_cast<const char*>(wr + (size_t)min(e0 + fr, E - 1) * dim) + 16 * fg;
-  f32x16_t acc;
+  // staging: thread tid moves bytes 16*(tid%8) of rows tid/8 + 32*i (i < 4) of both tiles
+  const int lc = tid & 7, lr = tid >> 3;
+  const char* xg[kRtPass];
+  const char* wg[kRtPass];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  uint4 a[3][4], b[3][4];
-  auto load = [&](uint4 (&da)[4], uint4 (&db)[4], int kt) {
+  for (int i = 0; i < kRtPass; ++i) {
+    xg[i] = reinterpret_cast<const char*>(x + (size_t)min(tb + lr + 32 * i, ntok - 1) * dim) + 16 * lc;
+    wg[i] = reinterpret_cast<const char*>(wr + (size_t)min(eb + lr + 32 * i, E - 1) * dim) + 16 * lc;
+  }
+  const int st_off = lr * kRtStride + 16 * lc;
+  uint4 rx[2][kRtPass], rw[2][kRtPass];
+  auto gload = [&](uint4 (&dx)[kRtPass], uint4 (&dw)[kRtPass], int kt) {
     kt = kt < k1 ? kt : k1 - 1;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      da[s] = ldg16(xa + kt * 128 + 32 * s);
-      db[s] = ldg16(wa + kt * 128 + 32 * s);
+    for (int i = 0; i < kRtPass; ++i) {
+      dx[i] = ldg16(xg[i] + kt * 128);
+      dw[i] = ldg16(wg[i] + kt * 128);
     }
   };
-  auto comp = [&](const uint4 (&da)[4], const uint4 (&db)[4]) {
+  auto sstore = [&](const uint4 (&dx)[kRtPass], const uint4 (&dw)[kRtPass], int buf) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, da[s]),
-                                                    __builtin_bit_cast(bf16x8_t, db[s]), acc, 0, 0, 0);
+    for (int i = 0; i < kRtPass; ++i) {
+      *reinterpret_cast<uint4*>(&sx[buf][st_off + 32 * i * kRtStride]) = dx[i];
+      *reinterpret_cast<uint4*>(&sw[buf][st_off + 32 * i * kRtStride]) = dw[i];
+    }
   };
-  load(a[0], b[0], k0);
-  load(a[1], b[1], k0 + 1);
+  // fragments: lane reads row (32j + lane%32) of its quarter, bytes 16*(lane/32) + 32s
+  const int fr = lane & 31, fg = lane >> 5;
+  const int xq = (64 * (wave & 1) + fr) * kRtStride + 16 * fg;
+  const int wq = (64 * (wave >> 1) + fr) * kRtStride + 16 * fg;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  auto comp = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 fa[2], fb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        fa[j] = *reinterpret_cast<const uint4*>(&sx[buf][xq + 32 * j * kRtStride + 32 * s]);
+        fb[j] = *reinterpret_cast<const uint4*>(&sw[buf][wq + 32 * j * kRtStride + 32 * s]);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[a]),
+                                                              __builtin_bit_cast(bf16x8_t, fb[b]),
+                                                              acc[a][b], 0, 0, 0);
+    }
+  };
+  gload(rx[0], rw[0], k0);
+  gload(rx[1], rw[1], k0 + 1);
+  sstore(rx[0], rw[0], 0);
+  __syncthreads();
+  // step kt: issue slice kt+2 into the registers slice kt held, multiply slice
+  // kt, store slice kt+1 into the other LDS buffer
   int kt = k0;
-  for (; kt + 3 <= k1; kt += 3) {
-    load(a[2], b[2], kt + 2);
-    comp(a[0], b[0]);
-    load(a[0], b[0], kt + 3);
-    comp(a[1], b[1]);
-    load(a[1], b[1], kt + 4);
-    comp(a[2], b[2]);
+  for (; kt + 2 <= k1; kt += 2) {
+    gload(rx[0], rw[0], kt + 2);
+    comp(0);
+    sstore(rx[1], rw[1], 1);
+    __syncthreads();
+    gload(rx[1], rw[1], kt + 3);
+    comp(1);
+    sstore(rx[0], rw[0], 0);
+    __syncthreads();
   }
-  if (kt < k1) comp(a[0], b[0]);
-  if (kt + 1 < k1) comp(a[1], b[1]);
+  if (kt < k1) comp(0);
 
   // D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane%32]: token row, expert column
-  const int e = e0 + fr;
-  if (e >= E) return;
   float* o = out + (size_t)blockIdx.z * split_stride;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = t0 + 8 * (i / 4) + 4 * fg + (i % 4);
-    if (t < ntok) o[(size_t)t * E + e] = acc[i];
+  for (int b = 0; b < 2; ++b) {
+    const int e = eb + 64 * (wave >> 1) + 32 * b + fr;
+    if (e >= E) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = tb + 64 * (wave & 1) + 32 * a + 8 * (i / 4) + 4 * fg + (i % 4);
+        if (t < ntok) o[(size_t)t * E + e] = acc[a][b][i];
+      }
   }
 }
 
