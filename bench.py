@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--config", default="c1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32)
-    ap.add_argument("--also", default="c2", help="extra configs timed after the main one ('' = none)")
+    ap.add_argument("--also", default="c0,c2,c3,c4",
+                    help="extra configs timed after the main one ('' = none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -114,26 +115,39 @@ def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False):
         moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
     torch.cuda.synchronize()
     moe.moe_profile_start(steps)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    t0.record(stream)
+    ev[0].record(stream)
     wall0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
-    t1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ncalls, up_ms, dn_ms = moe.moe_profile_stop()
-    ms = t0.elapsed_time(t1) / steps
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     c = counts.cpu().numpy()
-    res = dict(ms=ms, wall_ms=wall * 1e3 / steps, up_ms=up_ms / max(ncalls, 1),
+    res = dict(ms=ms, ms_median=per_step[len(per_step) // 2], ms_min=per_step[0],
+               wall_ms=wall * 1e3 / steps, up_ms=up_ms / max(ncalls, 1),
                down_ms=dn_ms / max(ncalls, 1), counts=c, **workload_numbers(cfg, c))
     if not want_layer:
         del dw, ws, x, y
         torch.cuda.empty_cache()
         return res, None
     return res, layer
+
+
+def floors(cfg, res):
+    """Roofline floor of one forward: max(algorithmic FLOPs / MFMA peak,
+    algorithmic bytes / HBM peak), and which one binds."""
+    dt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+    t_mfma = res["flops"] / (MFMA_PEAK_TFLOPS[dt] * 1e12) * 1e3
+    t_hbm = res["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3
+    return dict(t_floor_ms=round(max(t_mfma, t_hbm), 4), binding="mfma" if t_mfma > t_hbm else "hbm",
+                roofline_frac=round(max(t_mfma, t_hbm) / res["ms"], 4),
+                hbm_frac=round(res["bytes"] / (res["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                mfma_frac=round(res["flops"] / (res["ms"] / 1e3) / 1e12 / MFMA_PEAK_TFLOPS[dt], 4))
 
 
 def cpu_baseline(layer, ntok):
@@ -187,9 +201,7 @@ def main():
             "kernel": up_kernel_name(cfg),
             "kernel_ms": round(res["up_ms"], 4),
             "alg_bytes_per_launch": int(res["up_bytes"])}
-    layer_gbs = res["bytes"] / (res["ms"] / 1e3) / 1e9
     dt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
-    layer_tfs = res["flops"] / (res["ms"] / 1e3) / 1e12
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(res["ms"], 4),
@@ -200,10 +212,9 @@ def main():
                    "inter": cfg.inter, "shared_inter": cfg.inter_shared,
                    "active_experts": res["active_experts"]},
         "roofline": roof,
-        "layer": {"hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
-                  "mfma_frac": round(layer_tfs / MFMA_PEAK_TFLOPS[dt], 4),
-                  "alg_bytes": int(res["bytes"]), "alg_flops": int(res["flops"]),
-                  "down_ms": round(res["down_ms"], 4)},
+        "layer": {**floors(cfg, res), "ms_median": round(res["ms_median"], 4),
+                  "ms_min": round(res["ms_min"], 4), "alg_bytes": int(res["bytes"]),
+                  "alg_flops": int(res["flops"]), "down_ms": round(res["down_ms"], 4)},
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(layer, a.cpu_tokens)
@@ -212,11 +223,10 @@ def main():
     for name in [s for s in a.also.split(",") if s]:
         c2 = inputs.config_by_name(name)
         r2, _ = run_config(c2, max(5, a.steps // 2), a.warmup, torch, moe, inputs)
-        d2 = "fp8" if c2.w_dtype == "fp8" else c2.act_dtype
         extra[c2.name] = {
             "tokens_per_s": round(c2.T / (r2["ms"] / 1e3), 1), "ms_per_step": round(r2["ms"], 4),
-            "hbm_frac": round(r2["bytes"] / (r2["ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_frac": round(r2["flops"] / (r2["ms"] / 1e3) / 1e12 / MFMA_PEAK_TFLOPS[d2], 4),
+            "ms_median": round(r2["ms_median"], 4), "ms_min": round(r2["ms_min"], 4),
+            **floors(c2, r2),
             "up_kernel_ms": round(r2["up_ms"], 4), "down_kernel_ms": round(r2["down_ms"], 4),
             "up_kernel_hbm_frac": round(r2["up_bytes"] / (r2["up_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         }
