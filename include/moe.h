@@ -61,6 +61,24 @@ typedef enum moe_score {
   MOE_SCORE_SOFTMAX = 1
 } moe_score;
 
+/* Accumulator of the combine.
+ *   MOE_ACC_F32   ("Weighted expert sum", MoE.forward excerpt and its note:
+ *                 y starts as fp32 zeros): y_t = cast( sum_k w O + S ), fp32
+ *                 throughout, one cast at the end.
+ *   MOE_ACC_LAYER (the original DeepSeek-V3 MoE.forward in the hackaday.io log
+ *                 "Time to jump right in and swim with the big fish": y starts
+ *                 as zeros of x's dtype, experts are visited in ascending id and
+ *                 each does y[idx] += expert(x[idx]) * weights, then y + z with
+ *                 the shared output z): y_t = 0 in the layer dtype; for each of
+ *                 the token's experts in ascending id, y_t = cast(y_t + O*w)
+ *                 with the product and the sum in fp32 (torch's promotion of a
+ *                 bf16 tensor times fp32 weights); finally y_t = cast(y_t + S_t).
+ *                 With fp32 layers every cast is the identity.               */
+typedef enum moe_accumulate {
+  MOE_ACC_F32 = 0,
+  MOE_ACC_LAYER = 1
+} moe_accumulate;
+
 /* Shapes and hyper-parameters ("Expert scores", Gate constructor excerpt:
  * dim, topk = activated experts, n_groups, topk_groups = limited groups,
  * score_func, route_scale; routed and shared widths from the MoE constructor
@@ -86,6 +104,7 @@ typedef struct moe_params {
   int32_t act_dtype;     /* dtype of x and y: MOE_F32 or MOE_BF16                */
   int32_t router_dtype;  /* dtype of W_r (applied in fp32)                       */
   int32_t weight_dtype;  /* dtype of routed and shared expert weights            */
+  int32_t accumulate;    /* moe_accumulate of the combine (MOE_ACC_F32 default)  */
 } moe_params;
 
 /* Expert weights, device pointers.  The router weight is [E, dim] row-major.
@@ -162,7 +181,11 @@ moe_status moe_expert_ffn(const moe_params* p, int64_t T, const void* x,
  *   expert_out [T*topk, dim] act_dtype; row_of [T, topk]; topk_w [T, topk] fp32;
  *   shared_out [T, dim] or NULL.
  *   out y [T, dim] act_dtype = cast(sum_k topk_w[t,k] * expert_out[row_of[t,k]]
- *       + shared_out[t]); the k sum runs in slot order, in fp32. */
+ *       + shared_out[t]); the k sum visits the token's experts in ascending id
+ *       (ascending row, since rows are expert-contiguous; a token's rows must be
+ *       distinct) and adds the shared output last; each product and each sum
+ *       is rounded to fp32 (no fused multiply-add); MOE_ACC_LAYER also casts the
+ *       running sum to act_dtype after every addition. */
 moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
                        const int32_t* row_of, const float* topk_w, const void* shared_out,
                        void* y, void* stream);
@@ -220,7 +243,7 @@ const char* moe_last_error(void);
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t moe_abi_version(void);
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

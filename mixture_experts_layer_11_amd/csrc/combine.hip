@@ -4,11 +4,22 @@
 // MoE.forward excerpt: an fp32 accumulator, y[idx] += expert(x[idx]) * weight,
 // then the shared expert is added; cast back to the input dtype at the end).
 // Gather form: each token reads its topk rows of the expert outputs (found
-// through row_of), so there are no atomics and the sum order is fixed
-// (slot order, then the shared output).  Product then add, each rounded to
-// fp32, as the page's two-step update does.
+// through row_of), so there are no atomics and the sum order is fixed: the
+// token's experts in ascending id (the page's loop order), then the shared
+// output.  Product then add, each rounded to fp32, as the page's two-step
+// update does.
+// Layer-dtype form (the original DeepSeek-V3 MoE.forward, hackaday.io log
+// "Time to jump right in and swim with the big fish": y = zeros_like(x), a loop
+// over experts in ascending id doing y[idx] += expert(x[idx]) * weights, then
+// y + z): the slots are visited in ascending row - rows are expert-contiguous,
+// so that is ascending expert id - and the running sum is cast to the layer
+// dtype after every addition.
 #include "common.h"
 #include "kernels.h"
+
+// The page's update rounds the product and then the sum: no fused multiply-add
+// anywhere in this file (the compiler would otherwise contract them).
+#pragma clang fp contract(off)
 
 namespace moe {
 
@@ -44,6 +55,18 @@ template <> struct Vec8<float> {
   }
 };
 
+// Next slot of token t in ascending row order after row `prev` (a token's rows
+// are distinct; rows are expert-contiguous, so this is ascending expert id).
+__device__ __forceinline__ int next_slot(const int32_t* __restrict__ rt, const float* __restrict__ wt,
+                                         int topk, int prev, float& wk) {
+  int r = 0x7fffffff;
+  for (int k = 0; k < topk; ++k) {
+    const int rk = rt[k];
+    if (rk > prev && rk < r) { r = rk; wk = wt[k]; }
+  }
+  return r;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
                                                       const int32_t* __restrict__ row_of,
@@ -53,29 +76,77 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (col >= dim) return;
+  const int32_t* rt = row_of + (size_t)t * topk;
+  const float* wt = w + (size_t)t * topk;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < topk; ++k) {
-    const int r = row_of[(size_t)t * topk + k];
-    const float wk = w[(size_t)t * topk + k];
+  int r = -1;
+  for (int j = 0; j < topk; ++j) {
+    float wk = 0.f;
+    r = next_slot(rt, wt, topk, r, wk);
+    if (r == 0x7fffffff) break;   // repeated rows (invalid input): nothing left to add
     float v[8];
     Vec8<T>::load(out + (size_t)r * dim + col, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(v[i], wk));
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i] * wk;   // two roundings (contract off)
   }
   if (shared_out != nullptr) {
     float v[8];
     Vec8<T>::load(shared_out + (size_t)t * dim + col, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = __fadd_rn(acc[i], v[i]);
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i];
+  }
+  Vec8<T>::store(y + (size_t)t * dim + col, acc);
+}
+
+template <typename T> __device__ __forceinline__ float to_layer(float v);
+template <> __device__ __forceinline__ float to_layer<uint16_t>(float v) {
+  return __uint_as_float((uint32_t)f32_to_bf16(v) << 16);
+}
+template <> __device__ __forceinline__ float to_layer<float>(float v) { return v; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_layer_kernel(const T* __restrict__ out,
+                                                            const int32_t* __restrict__ row_of,
+                                                            const float* __restrict__ w,
+                                                            const T* __restrict__ shared_out,
+                                                            T* __restrict__ y, int dim, int topk) {
+  const int t = blockIdx.x;
+  const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+  if (col >= dim) return;
+  const int32_t* rt = row_of + (size_t)t * topk;
+  const float* wt = w + (size_t)t * topk;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int r = -1;
+  for (int j = 0; j < topk; ++j) {
+    float wk = 0.f;
+    r = next_slot(rt, wt, topk, r, wk);
+    if (r == 0x7fffffff) break;   // repeated rows (invalid input): nothing left to add
+    float v[8];
+    Vec8<T>::load(out + (size_t)r * dim + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = to_layer<T>(acc[i] + v[i] * wk);
+  }
+  if (shared_out != nullptr) {
+    float v[8];
+    Vec8<T>::load(shared_out + (size_t)t * dim + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i];
   }
   Vec8<T>::store(y + (size_t)t * dim + col, acc);
 }
 
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
                           const void* shared_out, void* y, int ntok, int dim, int topk,
-                          bool act_f32, hipStream_t st) {
+                          bool act_f32, bool layer_acc, hipStream_t st) {
   dim3 grid(ntok, (dim / 8 + 255) / 256);
-  if (act_f32)
+  if (layer_acc && act_f32)
+    combine_layer_kernel<float><<<grid, 256, 0, st>>>((const float*)expert_out, row_of, topk_w,
+                                                     (const float*)shared_out, (float*)y, dim, topk);
+  else if (layer_acc)
+    combine_layer_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)expert_out, row_of,
+                                                        topk_w, (const uint16_t*)shared_out,
+                                                        (uint16_t*)y, dim, topk);
+  else if (act_f32)
     combine_kernel<float><<<grid, 256, 0, st>>>((const float*)expert_out, row_of, topk_w,
                                                (const float*)shared_out, (float*)y, dim, topk);
   else

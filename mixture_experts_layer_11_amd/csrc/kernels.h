@@ -62,8 +62,10 @@ hipError_t launch_pack_weights(const uint8_t* src, int64_t rows, int64_t row_byt
                                hipStream_t st);
 
 // combine.hip
+// layer_acc: accumulate in the layer dtype over the experts in ascending id
+// (rows ascend with the expert id), casting after every addition.
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
                           const void* shared_out, void* y, int ntok, int dim, int topk,
-                          bool act_f32, hipStream_t st);
+                          bool act_f32, bool layer_acc, hipStream_t st);
 
 }  // namespace moe

@@ -106,6 +106,8 @@ moe_status validate(const moe_params* p, int64_t T) {
   if (p->topk > moe::kMaxTopk) return fail(MOE_ERR_UNSUPPORTED, "topk > 32");
   if (p->score_func != MOE_SCORE_SIGMOID && p->score_func != MOE_SCORE_SOFTMAX)
     return fail(MOE_ERR_INVALID_ARG, "unknown score_func");
+  if (p->accumulate != MOE_ACC_F32 && p->accumulate != MOE_ACC_LAYER)
+    return fail(MOE_ERR_INVALID_ARG, "unknown accumulate mode");
   if (p->dim < 1 || p->inter < 1 || p->shared_inter < 0)
     return fail(MOE_ERR_INVALID_ARG, "dim and inter must be >= 1, shared_inter >= 0");
   const bool f32 = p->act_dtype == MOE_F32 && p->router_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
@@ -330,7 +332,8 @@ moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
   if (T == 0) return MOE_OK;
   if (!expert_out || !row_of || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
   hipError_t e = moe::launch_combine(expert_out, row_of, topk_w, shared_out, y, (int)T, p->dim,
-                                     p->topk, p->act_dtype == MOE_F32, (hipStream_t)stream);
+                                     p->topk, p->act_dtype == MOE_F32,
+                                     p->accumulate == MOE_ACC_LAYER, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
@@ -385,7 +388,7 @@ moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_
   if ((s = do_permute(p, T, idx, cnt, off, st_tok, row_of, workspace, st)) != MOE_OK) return s;
   if ((s = do_ffn(p, T, x, st_tok, off, w, out, sh, workspace, st)) != MOE_OK) return s;
   hipError_t e = moe::launch_combine(out, row_of, wt, sh, y, (int)T, p->dim, p->topk,
-                                     p->act_dtype == MOE_F32, st);
+                                     p->act_dtype == MOE_F32, p->accumulate == MOE_ACC_LAYER, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 

@@ -37,10 +37,12 @@ class moe_params(ctypes.Structure):
                 ("topk", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("score_func", ctypes.c_int32),
                 ("route_scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("router_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32)]
+                ("router_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("accumulate", ctypes.c_int32)]
 
 
 _VP = ctypes.c_void_p
+_ACC = {"f32": 0, "layer": 1}
 
 
 class moe_weights(ctypes.Structure):
@@ -125,18 +127,19 @@ class Params:
     act_dtype: str
     router_dtype: str
     weight_dtype: str
+    accumulate: str = "f32"   # "f32" or "layer" (moe_accumulate)
 
     @staticmethod
     def from_config(cfg) -> "Params":
         return Params(cfg.dim, cfg.E, cfg.n_groups, cfg.topk_groups, cfg.topk, cfg.inter,
                       cfg.inter_shared, cfg.score_func, cfg.route_scale, cfg.act_dtype,
-                      cfg.router_dtype, cfg.w_dtype)
+                      cfg.router_dtype, cfg.w_dtype, getattr(cfg, "accumulate", "f32"))
 
     def c(self) -> moe_params:
         return moe_params(self.dim, self.n_experts, self.n_groups, self.topk_groups, self.topk,
                           self.inter, self.shared_inter, _SCORE[self.score_func],
                           self.route_scale, _DT[self.act_dtype], _DT[self.router_dtype],
-                          _DT[self.weight_dtype])
+                          _DT[self.weight_dtype], _ACC[self.accumulate])
 
     @property
     def act_torch(self):

@@ -35,6 +35,12 @@ also listed in the design notes):
      division, round to nearest even, saturating to +-448 (OCP e4m3fn).
   R5 softmax weights are not renormalised (only sigmoid is).
   R6 the shared expert is one MLP of inner width n_shared * inter.
+  R9 the accumulator is fp32 by default ([combine]); the original V3 class
+     ([v3], MoE.forward: y = zeros_like(x), y[idx] += expert(x[idx]) *
+     weights per expert in ascending id, return y + z) is the second mode
+     ("layer"): the running sum lives in the layer dtype, each update is
+     computed in fp32 (a bf16 tensor times fp32 weights promotes to fp32) and
+     cast back, and the shared output is added last with one more cast.
 """
 
 from __future__ import annotations
@@ -48,7 +54,8 @@ __all__ = [
     "bf16_round", "bf16_decode", "e4m3_table", "e4m3_decode", "e4m3_encode",
     "decode_weights", "quantize_act_1x128", "router_logits", "scores",
     "select_experts", "routing_weights", "gate", "permute", "swiglu",
-    "expert_ffn", "combine", "moe_forward", "moe_forward_dense", "brute_force_select",
+    "expert_ffn", "combine", "combine_layer", "round_to", "moe_forward", "moe_forward_dense",
+    "brute_force_select",
 ]
 
 F32 = np.float32
@@ -394,19 +401,43 @@ def combine(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out=None) -
     return y
 
 
+def combine_layer(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out,
+                  act_dtype: str) -> np.ndarray:
+    """[v3] MoE.forward with y held in the layer dtype (R9): y = 0; for each
+    expert in ascending id, y[t] = cast(y[t] + out[t,k] * w[t,k]) where the
+    product and the sum are fp32 and cast rounds to the layer dtype; then
+    y = cast(y + shared output).
+
+    outs [T, topk, dim] layer-dtype values; w [T, topk] fp32; idx [T, topk];
+    shared_out [T, dim] or None.  Returns fp64 values of the layer-dtype y.
+    """
+    T, K, dim = outs.shape
+    y = np.zeros((T, dim), dtype=F32)
+    order = np.argsort(idx, axis=1, kind="stable")            # ascending expert id per token
+    for j in range(K):
+        k = order[:, j]
+        o = outs[np.arange(T), k].astype(F32)
+        contrib = (o * w[np.arange(T), k][:, None].astype(F32)).astype(F32)
+        y = round_to((y + contrib).astype(F32), act_dtype).astype(F32)
+    if shared_out is not None:
+        y = round_to((y + np.asarray(shared_out).astype(F32)).astype(F32), act_dtype).astype(F32)
+    return y.astype(np.float64)
+
+
 def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_dtype,
                 router_dtype, E, n_groups, topk_groups, topk, score_func, route_scale,
-                tokens=None, route=None):
+                tokens=None, route=None, accumulate="f32"):
     """y = cast( sum_k w[t,k] * FFN_{idx[t,k]}(x_t) + FFN_shared(x_t) ).
 
     x, wr: storage-format arrays; expert_weights(e) -> (w1, w3, w2, w1_s, w3_s,
     w2_s); shared: the same tuple or None.  tokens: optional subset of token
     ids (the gate still runs on exactly those rows: routing is per token).
     route: optional (weights, idx) to use instead of the gate's own (for tokens
-    whose top-k is undecided within the margin).
+    whose top-k is undecided within the margin).  accumulate: "f32" ([combine])
+    or "layer" ([v3], R9).
 
     Returns dict(y=[n, dim] fp64 values of the cast output, y32=fp32
-    accumulator, w, idx, info).
+    accumulator (None in the layer mode), w, idx, info).
     """
     tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
     xv = decode_act(x[tok], act_dtype)
@@ -430,6 +461,11 @@ def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_d
     if shared is not None:
         w1, w3, w2, s1, s3, s2 = shared
         sh = expert_ffn(xv, w1, w3, w2, w_dtype, act_dtype, s1, s3, s2, xq)
+    if accumulate == "layer":
+        return {"y": combine_layer(outs, w, idx, sh, act_dtype), "y32": None, "w": w,
+                "idx": idx, "info": info, "tokens": tok}
+    if accumulate != "f32":
+        raise ValueError(accumulate)
     y = combine(outs, w, idx, sh)
     return {"y": round_to(y.astype(np.float64), act_dtype), "y32": y, "w": w, "idx": idx,
             "info": info, "tokens": tok}

@@ -26,10 +26,10 @@ def oracle_kwargs(cfg):
                 score_func=cfg.score_func, route_scale=cfg.route_scale)
 
 
-def run_oracle(layer, tokens=None, route=None):
+def run_oracle(layer, tokens=None, route=None, accumulate="f32"):
     return oracle.moe_forward(layer.x, layer.wr, layer.bias, expert_fn(layer),
                               shared_tuple(layer), tokens=tokens, route=route,
-                              **oracle_kwargs(layer.cfg))
+                              accumulate=accumulate, **oracle_kwargs(layer.cfg))
 
 
 def gate_oracle(layer, tokens=None):

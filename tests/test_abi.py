@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(moe.EXPORTS) == set(declared_functions())
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -72,6 +72,15 @@ def test_invalid_params_rejected_on_host(kw, status):
     s, _ = _ws_status(_p(**kw))
     assert s == status
     assert moe.lib().moe_last_error().decode() != ""
+
+
+def test_unknown_accumulate_mode_rejected():
+    pc = _p().c()
+    pc.accumulate = 7
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_workspace_size(ctypes.byref(pc), 16, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    pc.accumulate = 1
+    assert moe.lib().moe_workspace_size(ctypes.byref(pc), 16, ctypes.byref(n)) == moe.MOE_OK
 
 
 def test_workspace_size_grows_with_T_and_is_aligned():

@@ -217,16 +217,44 @@ def test_combine_parity(act):
     _sync()
     outs = vals[row_of]                                      # [T, K, dim]
     ref = oracle.moe_oracle.round_to(oracle.combine(outs, w, idx, shv).astype(np.float64), act)
-    mx, mean = rel_errors(moe.to_host_values(y), ref)
-    assert mx <= (1e-6 if act == "f32" else 8e-3) and mean <= (1e-7 if act == "f32" else 2e-4), (mx, mean)
+    # the same fp32 operations in the same order (ascending expert id, product
+    # then sum, shared last), so the result is bit-exact
+    np.testing.assert_array_equal(moe.to_host_values(y).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_combine_layer_accumulator_bitexact(act):
+    # same arithmetic in the same order (ascending expert id, a cast after every
+    # addition), so the result is bit-exact
+    rng = np.random.default_rng(6)
+    T, K, E, dim = 157, 8, 48, 256
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
+    counts, offsets, sorted_token, row_of = oracle.permute(idx, E)
+    vals = (rng.standard_normal((T * K, dim)) * 2.0).astype(np.float32)
+    shv = rng.standard_normal((T, dim)).astype(np.float32)
+    if act == "bf16":
+        vals_s, sh_s = inputs.f32_to_bf16_bits(vals), inputs.f32_to_bf16_bits(shv)
+        vals, shv = inputs.bf16_bits_to_f32(vals_s), inputs.bf16_bits_to_f32(sh_s)
+    else:
+        vals_s, sh_s = vals, shv
+    p = moe.Params(dim=dim, n_experts=E, n_groups=1, topk_groups=1, topk=K, inter=64,
+                   shared_inter=64, score_func="sigmoid", route_scale=1.0, act_dtype=act,
+                   router_dtype=act, weight_dtype=act, accumulate="layer")
+    y = moe.moe_combine(p, moe.to_device(vals_s, act), torch.from_numpy(row_of).to(DEV),
+                        torch.from_numpy(w).to(DEV), moe.to_device(sh_s, act))
+    _sync()
+    ref = oracle.combine_layer(vals[row_of], w, idx, shv, act)
+    np.testing.assert_array_equal(moe.to_host_values(y).astype(np.float64), ref)
 
 
 # ---------------------------------------------------------------------------
 # whole layer
 # ---------------------------------------------------------------------------
 
-def forward_and_check(cfg, layer, dw, tokens=None):
+def forward_and_check(cfg, layer, dw, tokens=None, accumulate="f32"):
     p = moe.Params.from_config(cfg)
+    p.accumulate = accumulate
     ws = moe.alloc_workspace(p, cfg.T)
     g_idx = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device=DEV)
     g_w = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device=DEV)
@@ -236,7 +264,7 @@ def forward_and_check(cfg, layer, dw, tokens=None):
     gi, gw = g_idx.cpu().numpy(), g_w.cpu().numpy()
     np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=cfg.E))
     tok = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
-    r = run_oracle(layer, tokens=tok)
+    r = run_oracle(layer, tokens=tok, accumulate=accumulate)
     same = check_routing(cfg, r["w"], r["idx"], r["info"], gi[tok], gw[tok], layer.bias)
     yv = moe.to_host_values(y)[tok]
     mx, mean = rel_errors(yv[same], r["y"][same])
@@ -248,6 +276,15 @@ def forward_and_check(cfg, layer, dw, tokens=None):
 def test_forward_parity(cfg, layers):
     layer, dw = layers(cfg)
     _, same = forward_and_check(cfg, layer, dw)
+    assert same.mean() > 0.97
+
+
+@pytest.mark.parametrize("ci", [0, 1, 3])
+def test_forward_parity_layer_accumulator(ci, layers):
+    # the original V3 combine (y in the layer dtype, experts in ascending id)
+    cfg = inputs.SMALL_CONFIGS[ci]
+    layer, dw = layers(cfg)
+    _, same = forward_and_check(cfg, layer, dw, accumulate="layer")
     assert same.mean() > 0.97
 
 

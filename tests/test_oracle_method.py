@@ -341,3 +341,75 @@ def test_fp8_expert_close_to_unquantised():
     ref = oracle.expert_ffn(x.astype(np.float64), a1, a3, a2, "f32", "f32")
     rel = np.abs(got - ref).sum() / np.abs(ref).sum()
     assert 1e-3 < rel < 0.1
+
+
+# ---------------------------------------------------------------------------
+# layer-dtype accumulator ([v3] MoE.forward; reading R9)
+# ---------------------------------------------------------------------------
+
+def _v3_statements_in_torch(outs, w, idx, shared, dtype):
+    """The original V3 class's combine run with torch on the CPU, statement by
+    statement: y = zeros_like(x); per expert in ascending id,
+    idx, top = where(indices == i); y[idx] += expert(x[idx]) * weights[idx, top, None];
+    then y + z.  The expert outputs are given (outs[t, k] = expert idx[t,k] of t)."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    T, K, dim = outs.shape
+    outs_t = torch.from_numpy(outs.astype(np.float32)).to(tdt)      # exact: values are layer dtype
+    weights = torch.from_numpy(w.astype(np.float32))
+    indices = torch.from_numpy(idx.astype(np.int64))
+    y = torch.zeros((T, dim), dtype=tdt)
+    for i in range(int(idx.max()) + 1):
+        rows, top = torch.where(indices == i)
+        if rows.numel() == 0:
+            continue
+        y[rows] += outs_t[rows, top] * weights[rows, top, None]
+    z = torch.from_numpy(shared.astype(np.float32)).to(tdt)
+    return (y + z).float().numpy().astype(np.float64)
+
+
+def check_combine_layer_matches_torch(dtype="bf16", seed=3):
+    rng = np.random.default_rng(seed)
+    T, E, K, dim = 37, 24, 6, 40
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.01, 1.5, (T, K)).astype(F32)
+    raw = rng.standard_normal((T, K, dim)) * 3.0
+    outs = oracle.round_to(raw, dtype)
+    shared = oracle.round_to(rng.standard_normal((T, dim)), dtype)
+    got = oracle.combine_layer(outs, w, idx, shared, dtype)
+    ref = _v3_statements_in_torch(outs, w, idx, shared, dtype)
+    np.testing.assert_array_equal(got, ref)
+    return got
+
+
+def test_combine_layer_matches_torch_v3_statements_bf16():
+    check_combine_layer_matches_torch("bf16")
+
+
+def test_combine_layer_matches_torch_v3_statements_f32():
+    check_combine_layer_matches_torch("f32", seed=4)
+
+
+def test_combine_layer_single_expert_is_identity():
+    rng = np.random.default_rng(9)
+    T, dim = 11, 16
+    outs = oracle.round_to(rng.standard_normal((T, 1, dim)), "bf16")
+    idx = rng.integers(0, 8, (T, 1)).astype(np.int32)
+    w = np.ones((T, 1), F32)
+    got = oracle.combine_layer(outs, w, idx, np.zeros((T, dim)), "bf16")
+    np.testing.assert_array_equal(got, outs[:, 0])
+
+
+def test_combine_layer_differs_from_fp32_accumulator_within_rounding():
+    # the two accumulators agree up to the extra bf16 roundings (K + 1 of them)
+    rng = np.random.default_rng(12)
+    T, E, K, dim = 64, 32, 8, 48
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, K)).astype(F32)
+    outs = oracle.round_to(rng.standard_normal((T, K, dim)), "bf16")
+    sh = oracle.round_to(rng.standard_normal((T, dim)), "bf16")
+    a = oracle.combine_layer(outs, w, idx, sh, "bf16")
+    b = oracle.round_to(oracle.combine(outs, w, idx, sh).astype(np.float64), "bf16")
+    scale = np.abs(outs).sum(1).max(-1, keepdims=True) + np.abs(sh).max(-1, keepdims=True)
+    assert np.all(np.abs(a - b) <= (K + 2) * 2.0 ** -8 * scale)
+    assert np.any(a != b)          # and they are different methods

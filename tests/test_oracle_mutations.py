@@ -127,3 +127,25 @@ def test_ties_away_from_zero_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "e4m3_encode", away)
     with pytest.raises(AssertionError):
         fmt.test_e4m3_midpoints_round_to_even_code()
+
+
+def test_layer_combine_without_per_step_rounding_is_caught(monkeypatch):
+    def late_cast(outs, w, idx, shared_out, act_dtype):
+        # mistake: fp32 running sum, one cast at the end
+        y = mo.combine(outs, w, idx, shared_out)
+        return mo.round_to(y.astype(np.float64), act_dtype)
+    _patch(monkeypatch, "combine_layer", late_cast)
+    with pytest.raises(AssertionError):
+        pins.check_combine_layer_matches_torch("bf16")
+
+
+def test_layer_combine_in_slot_order_is_caught(monkeypatch):
+    orig = mo.combine_layer
+
+    def slot_order(outs, w, idx, shared_out, act_dtype):
+        # mistake: visit the slots in their stored order instead of ascending expert id
+        fake = np.tile(np.arange(idx.shape[1], dtype=np.int32), (idx.shape[0], 1))
+        return orig(outs, w, fake, shared_out, act_dtype)
+    _patch(monkeypatch, "combine_layer", slot_order)
+    with pytest.raises(AssertionError):
+        pins.check_combine_layer_matches_torch("bf16")
