@@ -485,66 +485,69 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
 }
 
 // ---------------------------------------------------------------------------
-// fp8 stream tiles (prefill): the structure of the bf16 stream tiles with
-// one 128-wide K block - one scale block - per step, on
-// v_mfma_f32_16x16x128_f8f6f4 (one MFMA per block).  Block scales are applied
-// in fp32 outside the MFMA without a separate partial: the accumulator is
-// kept in units of the current block's scale s = w_scale * a_scale (> 0), so
-// each block is T <- mfma(W, X, T * s_prev / s) and the result is T * s_last,
-// the same sum as sum_kb s_kb * (W_kb X_kb) up to one fp32 rounding per block.  A operand
-// lane l: row l%16, bytes 32*(l/16)..+31 of the block; B likewise for the
-// token row; result D[4*(l/16)+i][l%16].  Each wave owns two 16-row weight
-// sub-tiles (up projection: W1 rows and the same rows of W3; down: 32 rows
-// of W2) against 128 token rows (8 sub-tiles).  Token slices carry their
-// per-row activation scale into LDS.  The up epilogue quantises h per 1x128
-// block: the 8 waves' 16-column slices of a token row form exactly one block,
-// so the amax is reduced across waves in LDS.
+// fp8 stream tiles (prefill), 192 tokens: the bf16 stream-tile layout (8 waves x 32
+// weight rows, W1 rows 0-15 and the same W3 rows 16-31 in one A tile, 32-row
+// token sub-tiles from LDS) on v_mfma_scale_f32_32x32x64_f8f6f4 - A lane l:
+// row l%32, bytes 32*(l/32)..+31 of a 64-byte K half; B likewise for the token
+// row; D as the bf16 32x32 tile, so D elements i < 8 are W1 rows (or the
+// first 16 W2 rows) and i >= 8 the W3 rows.  Two MFMAs per 128-wide K block.
+// Block scales: the accumulator is kept in units of the current block's
+// scale s = w_scale * a_scale (one s per half of the elements): each block
+// does acc <- mfma(W, X, acc * s_prev / s) and the result is acc * s_last, the
+// same sum as sum_kb s_kb * (W_kb X_kb) up to one fp32 rounding per block,
+// with no partial-product registers.  Token slices carry their per-row
+// activation scale into LDS.  The 32-row fragment pattern reads LDS without
+// bank conflicts (a 16x16x128 pattern conflicts on half its cycles), and 192
+// tokens cover most experts of an 8192-token batch in two m-tiles.  The up
+// epilogue quantises h per 1x128 block: the 8 waves' 16-column slices of a
+// token row form exactly one block, so the amax is reduced across waves in LDS.
 // ---------------------------------------------------------------------------
-using F8 = SCfg<128, 8, 4>;   // 128 tokens, 8 waves x 32 weight rows, ring of 4
-constexpr int kF8MT = F8::BM / 16;   // 16-row token sub-tiles
+using F8 = SCfg<192, 8, 2, 2>;   // 192 tokens, 8 waves x 32 weight rows, ring of 2
+constexpr int kF8MT = F8::BM / 32;
 
 struct StreamSrcF8 {
-  const char* x[F8::XLOADS];     // token rows (tid / 8) + 64*i, byte 16*(tid % 8) of the 128-byte block
-  const float* xs[F8::XLOADS];   // their activation scales, [row][K/128]
-  const char* w[2];              // this lane's rows of the two weight sub-tiles, at byte 32*(lane/16)
-  const float* ws[2];            // block scales of the two sub-tiles, [K/128]
+  const char* x[F8::XLOADS];    // token rows (tid / 8) + 64*i, byte 16*(tid % 8) of the 128-byte block
+  const float* xs[F8::XLOADS];  // their activation scales, [row][K/128]
+  const char* w;                 // this lane's weight row (tiled layout) at bytes 32*(lane/32) of a K half
+  const float* ws[2];            // block scales of the rows of D elements i < 8 and i >= 8, [K/128]
   int lds_st;
+  bool xact[F8::XLOADS];
 };
 
 template <int MT>
 __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (&sxs)[2][F8::BM],
-                                                 const StreamSrcF8& S, int nk,
-                                                 f32x4_t (&acc)[kF8MT][2]) {
-  // token load passes that reach the MT*16 rows this instantiation reads
-  constexpr int XL = std::min(F8::XLOADS, (16 * MT + F8::ROWS_PER_PASS - 1) / F8::ROWS_PER_PASS);
+                                                  const StreamSrcF8& S, int nk,
+                                                  f32x16_t (&acc)[kF8MT]) {
+  constexpr int XL = std::min(F8::XLOADS, (32 * MT + F8::ROWS_PER_PASS - 1) / F8::ROWS_PER_PASS);
   constexpr int RING = F8::RING;
-  const int lane = threadIdx.x & 63, fr = lane & 15, fg = lane >> 4;
-  i32x8_t_ wr[RING][2];          // [slice % RING][sub-tile]: 32 bytes per lane
-  float wsc[RING][2];
-  uint4 xr[2][XL];
-  float xsr[2][XL];
-  float sprev[MT][2];           // scale of the accumulator's current units
+  constexpr int UNROLL = std::lcm(RING, 2);
+  const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
+  i32x8_t_ wr[RING][2];          // [slice % RING][K half]
+  float wsc[RING][2];            // [slice % RING][D half]
+  uint4 xr[2][F8::XLOADS];
+  float xsr[2][F8::XLOADS];
+  float sprev[MT][2];            // units of the accumulator halves
 #pragma unroll
   for (int a = 0; a < MT; ++a) sprev[a][0] = sprev[a][1] = 1.f;
   auto wload = [&](i32x8_t_ (&dst)[2], float (&sc)[2], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint4 lo = ldg16(S.w[j] + kt * (2 * kChunkStride));   // bytes 32*(lane/16) + [0,16)
-      const uint4 hi = ldg16(S.w[j] + kt * (2 * kChunkStride) + 256);   // + [16,32)
+      const uint4 lo = ldg16(S.w + kt * (2 * kChunkStride) + j * kChunkStride);
+      const uint4 hi = ldg16(S.w + kt * (2 * kChunkStride) + j * kChunkStride + 256);
       dst[j] = i32x8_t_{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       sc[j] = S.ws[j][kt];
     }
   };
-  auto xload = [&](uint4 (&dst)[XL], float (&sc)[XL], int kt) {
+  auto xload = [&](uint4 (&dst)[F8::XLOADS], float (&sc)[F8::XLOADS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
       dst[i] = ldg16(S.x[i] + kt * 128);
-      sc[i] = S.xs[i][kt];       // the 8 lanes of a row load the same scale: no branch in the loop
+      sc[i] = S.xs[i][kt];       // the 8 lanes of a row load the same scale
     }
   };
-  auto xstore = [&](const uint4 (&src)[XL], const float (&sc)[XL], int buf) {
+  auto xstore = [&](const uint4 (&src)[F8::XLOADS], const float (&sc)[F8::XLOADS], int buf) {
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
       static_assert(F8::BM % F8::ROWS_PER_PASS == 0, "every token load pass lands inside the tile");
@@ -564,30 +567,29 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (
     xload(xr[r & 1], xsr[r & 1], kt + 2);
     wload(wr[(ws + RING - 1) % RING], wsc[(ws + RING - 1) % RING], kt + RING - 1);
     __builtin_amdgcn_sched_barrier(0);
-    // token sub-tile a+1 is read from LDS while sub-tile a is multiplied
     const char* sb = sx[r & 1] + fr * F8::STRIDE + 32 * fg;
     const float* sbs = sxs[r & 1] + fr;
-    i32x8_t_ bx[2];
-    float bs[2];
-    bx[0] = *reinterpret_cast<const i32x8_t_*>(sb);
-    bs[0] = sbs[0];
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
-      if (a + 1 < MT) {
-        bx[(a + 1) & 1] = *reinterpret_cast<const i32x8_t_*>(sb + 16 * (a + 1) * F8::STRIDE);
-        bs[(a + 1) & 1] = sbs[16 * (a + 1)];
-      }
+      i32x8_t_ bx[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float sc = wsc[ws][j] * bs[a & 1];
-        const float ratio = __builtin_amdgcn_rcpf(sc) * sprev[a][j];
-        sprev[a][j] = sc;
-        f32x4_t c = acc[a][j];
+      for (int j = 0; j < 2; ++j) bx[j] = *reinterpret_cast<const i32x8_t_*>(sb + 32 * a * F8::STRIDE + 64 * j);
+      const float xsc = sbs[32 * a];
+      float ratio[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] *= ratio;
-        acc[a][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wr[ws][j], bx[a & 1], c, 0, 0, 0, 127, 0, 127);
+      for (int h = 0; h < 2; ++h) {
+        const float sc = wsc[ws][h] * xsc;
+        ratio[h] = __builtin_amdgcn_rcpf(sc) * sprev[a][h];
+        sprev[a][h] = sc;
       }
-      __builtin_amdgcn_sched_barrier(0);
+      f32x16_t c = acc[a];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] *= ratio[i >> 3];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][j], bx[j], c, 0, 0, 0, 127, 0, 127);
+      acc[a] = c;
+      __builtin_amdgcn_sched_barrier(0);   // one token sub-tile's operands live at a time
     }
     xstore(xr[(r + 1) & 1], xsr[(r + 1) & 1], (r + 1) & 1);
     __syncthreads();
@@ -596,18 +598,16 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (
   auto tail = [&](int kt0, auto... R) {
     ((kt0 + decltype(R)::value < nk ? step(kt0 + decltype(R)::value, R) : void()), ...);
   };
-  const int nmain = nk - nk % F8::UNROLL;
+  const int nmain = nk - nk % UNROLL;
   int kt = 0;
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    for (; kt < nmain; kt += F8::UNROLL) body(kt, std::integral_constant<int, I>{}...);
+    for (; kt < nmain; kt += UNROLL) body(kt, std::integral_constant<int, I>{}...);
     tail(kt, std::integral_constant<int, I>{}...);
-  }(std::make_integer_sequence<int, F8::UNROLL>{});
+  }(std::make_integer_sequence<int, UNROLL>{});
 #pragma unroll
   for (int a = 0; a < MT; ++a)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[a][j][i] *= sprev[a][j];
+    for (int i = 0; i < 16; ++i) acc[a][i] *= sprev[a][i >> 3];
 }
 
 template <bool kUp>
@@ -631,6 +631,7 @@ void stream_fp8_kernel(FfnProblem p) {
 #pragma unroll
   for (int i = 0; i < F8::XLOADS; ++i) {
     const int tr = lr + F8::ROWS_PER_PASS * i;
+    S.xact[i] = tr < F8::BM;
     const int m = m0 + min(tr, rows_left - 1);
     size_t row;
     const uint8_t* base;
@@ -649,16 +650,15 @@ void stream_fp8_kernel(FfnProblem p) {
   }
   S.lds_st = lr * F8::STRIDE + 16 * lc;
 
-  const int fr = lane & 15, fg = lane >> 4;
+  const int fr = lane & 31, fg = lane >> 5;
   int ncol0;                      // up: first h column of the wave; down: first output column
   if (kUp) {
+    // A rows 0-15: W1 rows ncol0 + [0,16); rows 16-31: the same rows of W3
     ncol0 = ti.nt * F8::UPBN + wave * 16;          // N % 128 == 0: always inside
     const size_t eoff = shared ? 0 : (size_t)ti.g * N * K;
     const size_t soff = shared ? 0 : (size_t)ti.g * (N / 128) * KB;
-    const uint8_t* W1 = static_cast<const uint8_t*>(shared ? p.ws1 : p.w1) + eoff;
-    const uint8_t* W3 = static_cast<const uint8_t*>(shared ? p.ws3 : p.w3) + eoff;
-    S.w[0] = reinterpret_cast<const char*>(W1) + wtile_off(ncol0 + fr, 32 * fg, K);
-    S.w[1] = reinterpret_cast<const char*>(W3) + wtile_off(ncol0 + fr, 32 * fg, K);
+    const uint8_t* W = static_cast<const uint8_t*>(fr < 16 ? (shared ? p.ws1 : p.w1) : (shared ? p.ws3 : p.w3)) + eoff;
+    S.w = reinterpret_cast<const char*>(W) + wtile_off(ncol0 + (fr & 15), 32 * fg, K);
     S.ws[0] = (shared ? p.ws1s : p.w1s) + soff + (size_t)(ncol0 / 128) * KB;
     S.ws[1] = (shared ? p.ws3s : p.w3s) + soff + (size_t)(ncol0 / 128) * KB;
   } else {
@@ -666,70 +666,70 @@ void stream_fp8_kernel(FfnProblem p) {
     const int nrow = min(ncol0, N - 32);            // N % 128 == 0: a wave is all in or all out
     const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)ti.g * N * K);
     const float* W2s = (shared ? p.ws2s : p.w2s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nrow / 128) * KB;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      S.w[j] = reinterpret_cast<const char*>(W2) + wtile_off(nrow + 16 * j + fr, 32 * fg, K);
-      S.ws[j] = W2s;
-    }
+    S.w = reinterpret_cast<const char*>(W2) + wtile_off(nrow + fr, 32 * fg, K);
+    S.ws[0] = S.ws[1] = W2s;                        // 32 rows inside one 128-row block
   }
   const bool wave_active = ncol0 < N;
-  int m_active = (rows_left + 15) >> 4;
-  m_active = m_active > kF8MT ? kF8MT : m_active;   // the same for every wave (see the bf16 tiles)
+  int m_active = (rows_left + 31) >> 5;
+  m_active = m_active > kF8MT ? kF8MT : m_active;   // the same for every wave
 
-  f32x4_t acc[kF8MT][2];
+  f32x16_t acc[kF8MT];
 #pragma unroll
-  for (int a = 0; a < kF8MT; ++a) { acc[a][0] = f32x4_t{0.f, 0.f, 0.f, 0.f}; acc[a][1] = acc[a][0]; }
-  if (m_active > 6) stream_fp8_kloop<kF8MT>(sx, sxs, S, KB, acc);
-  else if (m_active > 4) stream_fp8_kloop<6>(sx, sxs, S, KB, acc);
-  else if (m_active > 2) stream_fp8_kloop<4>(sx, sxs, S, KB, acc);
-  else if (m_active > 1) stream_fp8_kloop<2>(sx, sxs, S, KB, acc);
-  else stream_fp8_kloop<1>(sx, sxs, S, KB, acc);
+  for (int a = 0; a < kF8MT; ++a)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((m_active == I + 1 ? stream_fp8_kloop<I + 1>(sx, sxs, S, KB, acc) : void()), ...);
+  }(std::make_integer_sequence<int, kF8MT>{});
 
-  // result lane layout: D[n = 4*(lane/16) + i][m = lane % 16]
-  const int ml = lane & 15, nl = 4 * (lane >> 4);
+  // D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
+  const int ml = lane & 31, rg = 4 * (lane >> 5);
   if (kUp) {
-    // h = silu(a1) * a3 for h columns ncol0 + nl + i; one 1x128 block per token row
+    // h = silu(a1) * a3 for h columns ncol0 + 8q + rg + i; the 8 waves' 16 columns
+    // of a token row form one 1x128 block, so its amax is reduced across waves
 #pragma unroll
     for (int a = 0; a < kF8MT; ++a) {
       float am = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(silu(acc[a][0][i]) * acc[a][1][i]));
-      am = fmaxf(am, __shfl_xor(am, 16, kWave));
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(silu(acc[a][i]) * acc[a][8 + i]));
       am = fmaxf(am, __shfl_xor(am, 32, kWave));
-      if (fg == 0) wamax[wave][16 * a + ml] = am;
+      if (fg == 0) wamax[wave][32 * a + ml] = am;
     }
     __syncthreads();
 #pragma unroll
     for (int a = 0; a < kF8MT; ++a) {
-      const int m = m0 + 16 * a + ml;
+      const int m = m0 + 32 * a + ml;
       if (a >= m_active || m >= ti.M) continue;
       float am = 0.f;
 #pragma unroll
-      for (int w = 0; w < F8::WAVES; ++w) am = fmaxf(am, wamax[w][16 * a + ml]);
+      for (int w = 0; w < F8::WAVES; ++w) am = fmaxf(am, wamax[w][32 * a + ml]);
       const float scale = am > 0.f ? __fdiv_rn(am, 448.0f) : 1.0f;
       const size_t row = shared ? (size_t)m : (size_t)(ti.row0 + m);
       uint8_t* hq = static_cast<uint8_t*>(shared ? p.hs : p.h) + row * N;
-      uint32_t pk = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = silu(acc[a][0][i]) * acc[a][1][i];
-        pk |= (uint32_t)f32_to_e4m3(__fdiv_rn(v, scale)) << (8 * i);
+      for (int q = 0; q < 2; ++q) {   // rows 8q + rg + [0,4) of W1, 16 + the same of W3
+        uint32_t pk = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = silu(acc[a][4 * q + i]) * acc[a][8 + 4 * q + i];
+          pk |= (uint32_t)f32_to_e4m3(__fdiv_rn(v, scale)) << (8 * i);
+        }
+        *reinterpret_cast<uint32_t*>(hq + ncol0 + 8 * q + rg) = pk;
       }
-      *reinterpret_cast<uint32_t*>(hq + ncol0 + nl) = pk;
       if (wave == 0 && fg == 0) (shared ? p.hsscale : p.hscale)[row * (N / 128) + ti.nt] = scale;
     }
   } else {
     if (!wave_active) return;
 #pragma unroll
     for (int a = 0; a < kF8MT; ++a) {
-      const int m = m0 + 16 * a + ml;
+      const int m = m0 + 32 * a + ml;
       if (a >= m_active || m >= ti.M) continue;
       uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) +
                        (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float v[4] = {acc[a][j][0], acc[a][j][1], acc[a][j][2], acc[a][j][3]};
-        store4<uint16_t>(orow + ncol0 + 16 * j + nl, v);
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[a][4 * q], acc[a][4 * q + 1], acc[a][4 * q + 2], acc[a][4 * q + 3]};
+        store4<uint16_t>(orow + ncol0 + 8 * q + rg, v);
       }
     }
   }
