@@ -148,7 +148,9 @@ moe_status moe_gate(const moe_params* p, int64_t T, const void* x, const void* w
 
 /* Dispatch ("Weighted expert sum", MoE.forward excerpt: bincount of the
  * indices, then per expert the (token, slot) pairs in row-major order).
- *   topk_idx [T, topk] int32, every id in [0, E) and distinct within a row.
+ *   topk_idx [T, topk] int32, every id in [0, E) and distinct within a row
+ *       (ids outside [0, E) are ignored; a repeated id in a row is placed once
+ *       and both slots get its row).
  *   out counts [E]: assignments per expert;
  *   out offsets [E+1]: exclusive prefix sum of counts (offsets[E] = T*topk);
  *   out sorted_token [T*topk]: token of each expert-contiguous row; inside an

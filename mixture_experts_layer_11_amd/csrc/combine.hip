@@ -55,47 +55,27 @@ template <> struct Vec8<float> {
   }
 };
 
-// Next slot of token t in ascending row order after row `prev` (a token's rows
-// are distinct; rows are expert-contiguous, so this is ascending expert id).
-__device__ __forceinline__ int next_slot(const int32_t* __restrict__ rt, const float* __restrict__ wt,
-                                         int topk, int prev, float& wk) {
-  int r = 0x7fffffff;
-  for (int k = 0; k < topk; ++k) {
-    const int rk = rt[k];
-    if (rk > prev && rk < r) { r = rk; wk = wt[k]; }
-  }
-  return r;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
-                                                      const int32_t* __restrict__ row_of,
-                                                      const float* __restrict__ w,
-                                                      const T* __restrict__ shared_out,
-                                                      T* __restrict__ y, int dim, int topk) {
-  const int t = blockIdx.x;
-  const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
-  if (col >= dim) return;
-  const int32_t* rt = row_of + (size_t)t * topk;
-  const float* wt = w + (size_t)t * topk;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int r = -1;
-  for (int j = 0; j < topk; ++j) {
-    float wk = 0.f;
-    r = next_slot(rt, wt, topk, r, wk);
-    if (r == 0x7fffffff) break;   // repeated rows (invalid input): nothing left to add
-    float v[8];
-    Vec8<T>::load(out + (size_t)r * dim + col, v);
+// A token's slots in ascending row order (rows are expert-contiguous, so this
+// is ascending expert id): the rows and weights of at most KMAX slots are
+// loaded into registers and sorted by a fully unrolled exchange network
+// (compile-time indices, so nothing leaves the registers).  Unused slots get
+// row INT_MAX and sort last.
+template <int KMAX>
+__device__ __forceinline__ void sorted_slots(const int32_t* __restrict__ rt, const float* __restrict__ wt,
+                                             int topk, int (&r)[KMAX], float (&w)[KMAX]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i] * wk;   // two roundings (contract off)
+  for (int k = 0; k < KMAX; ++k) {
+    r[k] = k < topk ? rt[k] : 0x7fffffff;
+    w[k] = k < topk ? wt[k] : 0.f;
   }
-  if (shared_out != nullptr) {
-    float v[8];
-    Vec8<T>::load(shared_out + (size_t)t * dim + col, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i];
-  }
-  Vec8<T>::store(y + (size_t)t * dim + col, acc);
+  for (int i = 0; i < KMAX; ++i)
+#pragma unroll
+    for (int j = i + 1; j < KMAX; ++j)
+      if (r[j] < r[i]) {
+        const int tr = r[i]; r[i] = r[j]; r[j] = tr;
+        const float tw = w[i]; w[i] = w[j]; w[j] = tw;
+      }
 }
 
 template <typename T> __device__ __forceinline__ float to_layer(float v);
@@ -104,27 +84,32 @@ template <> __device__ __forceinline__ float to_layer<uint16_t>(float v) {
 }
 template <> __device__ __forceinline__ float to_layer<float>(float v) { return v; }
 
-template <typename T>
-__global__ __launch_bounds__(256) void combine_layer_kernel(const T* __restrict__ out,
-                                                            const int32_t* __restrict__ row_of,
-                                                            const float* __restrict__ w,
-                                                            const T* __restrict__ shared_out,
-                                                            T* __restrict__ y, int dim, int topk) {
+// kLayer = false: fp32 running sum, one cast at the end; true: the running
+// sum is cast to the layer dtype after every addition.
+template <typename T, int KMAX, bool kLayer>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ w,
+                                                      const T* __restrict__ shared_out,
+                                                      T* __restrict__ y, int dim, int topk) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (col >= dim) return;
-  const int32_t* rt = row_of + (size_t)t * topk;
-  const float* wt = w + (size_t)t * topk;
+  int rs[KMAX];
+  float ws[KMAX];
+  sorted_slots<KMAX>(row_of + (size_t)t * topk, w + (size_t)t * topk, topk, rs, ws);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int r = -1;
-  for (int j = 0; j < topk; ++j) {
-    float wk = 0.f;
-    r = next_slot(rt, wt, topk, r, wk);
-    if (r == 0x7fffffff) break;   // repeated rows (invalid input): nothing left to add
-    float v[8];
-    Vec8<T>::load(out + (size_t)r * dim + col, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = to_layer<T>(acc[i] + v[i] * wk);
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < topk) {
+      float v[8];
+      Vec8<T>::load(out + (size_t)rs[j] * dim + col, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float a = acc[i] + v[i] * ws[j];   // two roundings (contract off)
+        acc[i] = kLayer ? to_layer<T>(a) : a;
+      }
+    }
   }
   if (shared_out != nullptr) {
     float v[8];
@@ -135,24 +120,25 @@ __global__ __launch_bounds__(256) void combine_layer_kernel(const T* __restrict_
   Vec8<T>::store(y + (size_t)t * dim + col, acc);
 }
 
+template <typename T, bool kLayer>
+static void launch_combine_t(dim3 grid, hipStream_t st, const void* out, const int32_t* row_of,
+                             const float* w, const void* shared_out, void* y, int dim, int topk) {
+  if (topk <= 8)
+    combine_kernel<T, 8, kLayer><<<grid, 256, 0, st>>>((const T*)out, row_of, w, (const T*)shared_out,
+                                                       (T*)y, dim, topk);
+  else
+    combine_kernel<T, kMaxTopk, kLayer><<<grid, 256, 0, st>>>((const T*)out, row_of, w,
+                                                              (const T*)shared_out, (T*)y, dim, topk);
+}
+
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
                           const void* shared_out, void* y, int ntok, int dim, int topk,
                           bool act_f32, bool layer_acc, hipStream_t st) {
   dim3 grid(ntok, (dim / 8 + 255) / 256);
-  if (layer_acc && act_f32)
-    combine_layer_kernel<float><<<grid, 256, 0, st>>>((const float*)expert_out, row_of, topk_w,
-                                                     (const float*)shared_out, (float*)y, dim, topk);
-  else if (layer_acc)
-    combine_layer_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)expert_out, row_of,
-                                                        topk_w, (const uint16_t*)shared_out,
-                                                        (uint16_t*)y, dim, topk);
-  else if (act_f32)
-    combine_kernel<float><<<grid, 256, 0, st>>>((const float*)expert_out, row_of, topk_w,
-                                               (const float*)shared_out, (float*)y, dim, topk);
-  else
-    combine_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)expert_out, row_of, topk_w,
-                                                  (const uint16_t*)shared_out, (uint16_t*)y, dim,
-                                                  topk);
+  if (act_f32 && layer_acc) launch_combine_t<float, true>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
+  else if (act_f32) launch_combine_t<float, false>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
+  else if (layer_acc) launch_combine_t<uint16_t, true>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
+  else launch_combine_t<uint16_t, false>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
   return hipGetLastError();
 }
 

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const T* __restrict_
 // tiles go through LDS in 64-element K slices, double-buffered, each slice
 // loaded into registers two steps ahead.  When the tiles alone cannot fill
 // the GPU, K is split over blockIdx.z; the split partials go to a workspace
-// and are summed in split order by router_reduce_kernel, so the result does
-// not depend on timing.
+// and the selection kernel sums them in split order as it reads them, so the
+// result does not depend on timing.
 // ---------------------------------------------------------------------------
 constexpr int kRtTile = 128;              // tokens and experts per workgroup
 constexpr int kRtStride = 144;            // LDS bytes per 128-byte row slice (padded)
@@ -196,17 +196,6 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __r
   }
 }
 
-// logits[i] = sum over splits s = 0, 1, ... of part[s][i], in that order
-__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part, int S,
-                                                            size_t n, float* __restrict__ logits) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    float v = part[i];
-    for (int s = 1; s < S; ++s) v += part[(size_t)s * n + i];
-    logits[i] = v;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Selection: one wave per token.
 //   s = sigmoid(z) or softmax(z); s' = s + bias (selection only)
@@ -220,8 +209,10 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
 constexpr int kSelWaves = 4;
 constexpr int kMaxPerLane = 8;
 
+// `logits` holds `splits` partial logit arrays of ntok*E values each (one when
+// the router did not split K); they are summed in split order, in fp32.
 __global__ __launch_bounds__(256) void gate_select_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int ntok, int E,
+    const float* __restrict__ logits, int splits, const float* __restrict__ bias, int ntok, int E,
     int n_groups, int topk_groups, int topk, int score_softmax, float route_scale,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   __shared__ float sel[kSelWaves][512];
@@ -234,10 +225,22 @@ __global__ __launch_bounds__(256) void gate_select_kernel(
 
   float s[kMaxPerLane], sp[kMaxPerLane];
   const float* zrow = logits + (size_t)tt * E;
+  const size_t stride = (size_t)ntok * E;
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const int e = lane + 64 * j;
-    s[j] = e < E ? zrow[e] : 0.f;
+  for (int j = 0; j < kMaxPerLane; ++j) s[j] = lane + 64 * j < E ? zrow[lane + 64 * j] : 0.f;
+  for (int q0 = 1; q0 < splits; q0 += 4) {   // 4 splits' loads in flight, summed in split order
+    float v[4][kMaxPerLane];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j) {
+        const int e = lane + 64 * j;
+        v[qq][j] = (q0 + qq < splits && e < E) ? zrow[(size_t)(q0 + qq) * stride + e] : 0.f;
+      }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j) s[j] += v[qq][j];
   }
   if (score_softmax) {
     float m = -INFINITY;
@@ -355,15 +358,19 @@ hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bia
     dim3 g((ntok + kRtTile - 1) / kRtTile, (E + kRtTile - 1) / kRtTile, S);
     router_mfma_kernel<<<g, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr,
                                           S > 1 ? rpart : logits, ntok, dim, E, per, n);
-    if (S > 1) {
-      const size_t blocks = (n + 255) / 256;
-      router_reduce_kernel<<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(rpart, S, n, logits);
+    if (S > 1) {   // the selection sums the split partials as it reads them
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      gate_select_kernel<<<(ntok + kSelWaves - 1) / kSelWaves, 256, 0, st>>>(
+          rpart, S, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0, route_scale,
+          topk_idx, topk_w);
+      return hipGetLastError();
     }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   gate_select_kernel<<<(ntok + kSelWaves - 1) / kSelWaves, 256, 0, st>>>(
-      logits, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0, route_scale,
+      logits, 1, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0, route_scale,
       topk_idx, topk_w);
   return hipGetLastError();
 }

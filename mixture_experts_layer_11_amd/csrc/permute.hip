@@ -3,8 +3,8 @@
 // Source: "DeepSeek-V3.2-Exp · Weighted expert sum", MoE.forward excerpt: a
 // bincount of the chosen indices, then per expert the (token, slot) pairs in
 // the row-major order torch.where yields.  Here: a blocked counting sort.
-//   count  : per block of kPermBlock tokens, per-expert counts (LDS atomics;
-//            the totals do not depend on their order)
+//   count  : per block of kPermBlock tokens, per-expert bit masks of the
+//            block's tokens (LDS atomic OR), counted by popcount
 //   scan   : per expert, exclusive prefix over blocks; then exclusive prefix
 //            over experts -> counts, offsets, and each block's base row
 //   scatter: per block, a bit mask per expert of the block's tokens that
@@ -24,18 +24,25 @@ constexpr int kPermWords = kPermBlock / 64;   // 64-bit mask words per expert
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx,
                                                             int ntok, int topk, int E,
                                                             int32_t* __restrict__ blk_count) {
-  __shared__ int hist[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  // per-expert bit masks of the block's tokens (the scatter builds the same
+  // masks), counted by popcount: a repeated id in a row counts once
+  __shared__ unsigned long long mask[kMaxExperts][kPermWords];
+  for (int i = threadIdx.x; i < E * kPermWords; i += blockDim.x) (&mask[0][0])[i] = 0ull;
   __syncthreads();
   const int t0 = blockIdx.x * kPermBlock;
   const int n = min(kPermBlock, ntok - t0) * topk;
   const int32_t* p = idx + (size_t)t0 * topk;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int e = p[i];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    const int e = p[i], t = i / topk;
+    if (e >= 0 && e < E) atomicOr(&mask[e][t >> 6], 1ull << (t & 63));
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) blk_count[(size_t)blockIdx.x * E + e] = hist[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWords; ++w) c += __popcll(mask[e][w]);
+    blk_count[(size_t)blockIdx.x * E + e] = c;
+  }
 }
 
 // single workgroup of 1024 threads (E <= kMaxExperts <= 1024)
@@ -102,6 +109,57 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   }
 }
 
+// All three steps in one workgroup when the tokens fit one block (decode):
+// the same counting sort without the block-count round trip through global
+// memory and without two launches.
+__global__ __launch_bounds__(1024) void permute_one_block_kernel(const int32_t* __restrict__ idx,
+                                                                 int ntok, int topk, int E,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ sorted_token,
+                                                                 int32_t* __restrict__ row_of) {
+  __shared__ int buf[1024];
+  __shared__ int base[kMaxExperts];
+  __shared__ unsigned long long mask[kMaxExperts][kPermWords];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kPermWords; i += blockDim.x) (&mask[0][0])[i] = 0ull;
+  __syncthreads();
+  const int n = ntok * topk;
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int e = idx[i], t = i / topk;
+    if (e >= 0 && e < E) atomicOr(&mask[e][t >> 6], 1ull << (t & 63));
+  }
+  __syncthreads();
+  // per-expert count = popcount of its mask; exclusive scan over experts
+  int total = 0;
+  if (tid < E)
+    for (int w = 0; w < kPermWords; ++w) total += __popcll(mask[tid][w]);
+  buf[tid] = tid < E ? total : 0;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? buf[tid - o] : 0;
+    __syncthreads();
+    buf[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    base[tid] = buf[tid] - total;
+    counts[tid] = total;
+    offsets[tid] = buf[tid] - total;
+    if (tid == E - 1) offsets[E] = buf[tid];
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int e = idx[i], t = i / topk, k = i - t * topk;
+    if (e < 0 || e >= E) continue;
+    int rank = __popcll(mask[e][t >> 6] & ((1ull << (t & 63)) - 1ull));
+    for (int w = 0; w < (t >> 6); ++w) rank += __popcll(mask[e][w]);
+    const int pos = base[e] + rank;
+    sorted_token[pos] = t;
+    row_of[(size_t)t * topk + k] = pos;
+  }
+}
+
 size_t permute_scratch_bytes(int ntok, int E) {
   const size_t nblk = (size_t)(ntok + kPermBlock - 1) / kPermBlock;
   return nblk * (size_t)E * sizeof(int32_t);
@@ -111,6 +169,11 @@ hipError_t launch_permute(const int32_t* idx, int ntok, int topk, int E, int32_t
                           int32_t* offsets, int32_t* sorted_token, int32_t* row_of,
                           int32_t* scratch, hipStream_t st) {
   const int nblk = (ntok + kPermBlock - 1) / kPermBlock;
+  if (nblk == 1) {
+    permute_one_block_kernel<<<1, 1024, 0, st>>>(idx, ntok, topk, E, counts, offsets, sorted_token,
+                                                 row_of);
+    return hipGetLastError();
+  }
   permute_count_kernel<<<nblk, 256, 0, st>>>(idx, ntok, topk, E, scratch);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -91,6 +91,7 @@ def test_gate_parity(cfg):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,E,K", [(1, 8, 2), (63, 16, 4), (64, 16, 4), (65, 32, 8),
+                                   (128, 256, 8), (256, 512, 32), (257, 256, 8),
                                    (1000, 256, 8), (4096, 256, 8), (8192, 64, 6),
                                    (777, 512, 32), (300, 3, 3)])
 def test_permute_bitexact(T, E, K):
@@ -196,9 +197,10 @@ def test_pack_weights_bitexact(rows, row_bytes):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("act", ["bf16", "f32"])
-def test_combine_parity(act):
-    rng = np.random.default_rng(5)
-    T, K, E, dim = 203, 6, 40, 320
+@pytest.mark.parametrize("K", [6, 12])          # the 8-slot and the 32-slot kernels
+def test_combine_parity(act, K):
+    rng = np.random.default_rng(5 + K)
+    T, E, dim = 203, 40, 320
     idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
     w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
     counts, offsets, sorted_token, row_of = oracle.permute(idx, E)
@@ -223,11 +225,12 @@ def test_combine_parity(act):
 
 
 @pytest.mark.parametrize("act", ["bf16", "f32"])
-def test_combine_layer_accumulator_bitexact(act):
+@pytest.mark.parametrize("K", [8, 20])
+def test_combine_layer_accumulator_bitexact(act, K):
     # same arithmetic in the same order (ascending expert id, a cast after every
     # addition), so the result is bit-exact
-    rng = np.random.default_rng(6)
-    T, K, E, dim = 157, 8, 48, 256
+    rng = np.random.default_rng(6 + K)
+    T, E, dim = 157, 48, 256
     idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
     w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
     counts, offsets, sorted_token, row_of = oracle.permute(idx, E)
