@@ -298,6 +298,7 @@ struct SCfg {
   static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), 2);   // steps with compile-time stage indices
 };
 using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
+using SHuge = SCfg<256, 8, 2, 2>; // experts of many hundred tokens: larger tiles, shallower rings
 using SMid = SCfg<64, 4, 4>;   // 64-token tiles, three workgroups per CU
 
 template <class C>
@@ -743,6 +744,13 @@ void stream_bf16_kernel(FfnProblem p) {
 }
 
 template <bool kUp>
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void stream_huge_bf16_kernel(FfnProblem p) {
+  __shared__ __attribute__((aligned(16))) char sx[2][SHuge::LDS];
+  stream_tile<SHuge, kUp>(p, sx);
+}
+
+template <bool kUp>
 __global__ __launch_bounds__(256, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void stream_mid_bf16_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[2][SMid::LDS];
@@ -975,7 +983,7 @@ size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool ac
   return ((size_t)ntok * topk * inter + (size_t)ntok * inter_s) * esz;
 }
 
-enum class Tiles { Skinny, Mid, Big };
+enum class Tiles { Skinny, Mid, Big, Huge };
 
 // Tile shape for a batch: 16-token skinny tiles while experts average few
 // rows (weight streaming, no reuse to gain), 64-token tiles with several
@@ -986,6 +994,7 @@ static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
   if (p.wkind == WKind::FP8) return R >= 48L * p.E ? Tiles::Big : Tiles::Skinny;
   if (p.wkind != WKind::BF16) return Tiles::Skinny;
   if (p.dim % 64 || p.inter % 64 || (has_shared && p.inter_s % 64)) return Tiles::Skinny;
+  if (R >= 384L * p.E) return Tiles::Huge;
   if (R >= 128L * p.E) return Tiles::Big;
   if (R >= 48L * p.E) return Tiles::Mid;
   return Tiles::Skinny;
@@ -998,6 +1007,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const bool f8 = p.wkind == WKind::FP8;
   int bm = 16, bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
   if (t == Tiles::Big && f8) bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN;
+  else if (t == Tiles::Huge) bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN;
   else if (t == Tiles::Big) bm = SBig::BM, bn_up = SBig::UPBN, bn_dn = SBig::BN;
   else if (t == Tiles::Mid) bm = SMid::BM, bn_up = SMid::UPBN, bn_dn = SMid::BN;
   const int nt_up = ceil_div(p.inter, bn_up), nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
@@ -1019,6 +1029,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   }
   mark(0);
   if (t == Tiles::Big && f8) stream_fp8_kernel<true><<<g_up, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Huge) stream_huge_bf16_kernel<true><<<g_up, SHuge::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big) stream_bf16_kernel<true><<<g_up, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_mid_bf16_kernel<true><<<g_up, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
@@ -1028,6 +1039,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   mark(2);
   if (t == Tiles::Big && f8) stream_fp8_kernel<false><<<g_dn, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Huge) stream_huge_bf16_kernel<false><<<g_dn, SHuge::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big) stream_bf16_kernel<false><<<g_dn, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_mid_bf16_kernel<false><<<g_dn, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);

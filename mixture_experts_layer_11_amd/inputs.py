@@ -131,6 +131,10 @@ SMALL_CONFIGS = [
               topk=2, score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=640,
               inter_shared=384, act_dtype="bf16", w_dtype="fp8", router_dtype="bf16",
               seed=12008),
+    MoEConfig("s9_mini_bf16_large_experts", T=1200, dim=384, E=8, n_groups=2, topk_groups=1,
+              topk=4, score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=320,
+              inter_shared=192, act_dtype="bf16", w_dtype="bf16", router_dtype="bf16",
+              seed=12009),
 ]
 
 
