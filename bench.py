@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--also", default="c0,c2,c3,c4",
                     help="extra configs timed after the main one ('' = none)")
+    ap.add_argument("--experts", default="",
+                    help="b:e - time one expert-parallel rank's share: only routed experts b..e-1 "
+                         "(their weights alone are uploaded); the gate still covers all experts")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -66,8 +69,13 @@ def up_kernel_name(cfg):
     return "moe::up_skinny_kernel<%s>" % ("float" if cfg.w_dtype == "f32" else "unsigned short")
 
 
-def workload_numbers(cfg, counts):
-    """Algorithmic FLOPs and bytes of one forward, and of the up-projection launch."""
+def workload_numbers(cfg, counts, experts=None):
+    """Algorithmic FLOPs and bytes of one forward, and of the up-projection launch
+    (experts=(b, e): only the routed experts of that range)."""
+    if experts is not None:
+        counts = counts.copy()
+        counts[:experts[0]] = 0
+        counts[experts[1]:] = 0
     wsz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w_dtype]
     asz = 4 if cfg.act_dtype == "f32" else 2
     rsz = 4 if cfg.router_dtype == "f32" else 2
@@ -78,12 +86,13 @@ def workload_numbers(cfg, counts):
         scale_b = 4 * (dim // 128) * (I // 128)          # per matrix per expert
     per_expert = 3 * (I * dim * wsz + scale_b)
     shared = 3 * Is * dim * wsz + (3 * 4 * (dim // 128) * (Is // 128) if cfg.w_dtype == "fp8" else 0)
-    flops = 2 * T * E * dim + 2 * T * K * 3 * dim * I + 2 * T * 3 * dim * Is
+    routed_rows = int(counts.sum())                         # T * K for the full range
+    flops = 2 * T * E * dim + 2 * routed_rows * 3 * dim * I + 2 * T * 3 * dim * Is
     bytes_ = active * per_expert + shared + E * dim * rsz + T * dim * asz * 2
     hsz = 1 if cfg.w_dtype == "fp8" else asz
     up_bytes = (active * 2 * (I * dim * wsz + scale_b) + 2 * (Is * dim * wsz) + T * dim * asz
-                + (T * K * I + T * Is) * hsz)
-    up_flops = 2 * T * K * 2 * dim * I + 2 * T * 2 * dim * Is
+                + (routed_rows * I + T * Is) * hsz)
+    up_flops = 2 * routed_rows * 2 * dim * I + 2 * T * 2 * dim * Is
     return dict(active_experts=active, flops=flops, bytes=bytes_, up_bytes=up_bytes,
                 up_flops=up_flops, per_expert_up_bytes=2 * (I * dim * wsz + scale_b))
 
@@ -104,10 +113,12 @@ def traffic_for(kernel, workload):
     return ent["hbm_bytes_per_launch"]
 
 
-def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False):
+def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False, experts=None):
     layer = inputs.draw_layer(cfg)
-    dw = moe.upload_layer(layer)
+    dw = moe.upload_layer(layer, experts=experts)
     p = moe.Params.from_config(cfg)
+    if experts is not None:
+        p.expert_begin, p.expert_end = experts
     ws = moe.alloc_workspace(p, cfg.T)
     x = moe.to_device(layer.x, cfg.act_dtype)
     y = torch.empty((cfg.T, cfg.dim), dtype=p.act_torch, device="cuda")
@@ -132,7 +143,7 @@ def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False):
     c = counts.cpu().numpy()
     res = dict(ms=ms, ms_median=per_step[len(per_step) // 2], ms_min=per_step[0],
                wall_ms=wall * 1e3 / steps, up_ms=up_ms / max(ncalls, 1),
-               down_ms=dn_ms / max(ncalls, 1), counts=c, **workload_numbers(cfg, c))
+               down_ms=dn_ms / max(ncalls, 1), counts=c, **workload_numbers(cfg, c, experts))
     if not want_layer:
         del dw, ws, x, y
         torch.cuda.empty_cache()
@@ -194,10 +205,12 @@ def main():
     from mixture_experts_layer_11_amd import inputs, moe
     moe.lib()
     cfg = inputs.config_by_name(a.config)
-    res, layer = run_config(cfg, a.steps, a.warmup, torch, moe, inputs, want_layer=True)
+    experts = tuple(int(v) for v in a.experts.split(":")) if a.experts else None
+    res, layer = run_config(cfg, a.steps, a.warmup, torch, moe, inputs, want_layer=True,
+                            experts=experts)
     tok_s = cfg.T / (res["ms"] / 1e3)
     up_gbs = res["up_bytes"] / (res["up_ms"] / 1e3) / 1e9
-    traffic = traffic_for("up_grouped_gemm", cfg.name)
+    traffic = None if experts else traffic_for("up_grouped_gemm", cfg.name)
     roof = {"bound": "hbm", "achieved": round(up_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(up_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": up_kernel_name(cfg),
@@ -212,13 +225,14 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "dim": cfg.dim, "n_experts": cfg.E,
                    "topk": cfg.topk, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
                    "inter": cfg.inter, "shared_inter": cfg.inter_shared,
-                   "active_experts": res["active_experts"]},
+                   "active_experts": res["active_experts"],
+                   **({"expert_range": list(experts)} if experts else {})},
         "roofline": roof,
         "layer": {**floors(cfg, res), "ms_median": round(res["ms_median"], 4),
                   "ms_min": round(res["ms_min"], 4), "alg_bytes": int(res["bytes"]),
                   "alg_flops": int(res["flops"]), "down_ms": round(res["down_ms"], 4)},
     }
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not experts:
         out["cpu_baseline"] = cpu_baseline(layer, a.cpu_tokens)
     del layer
     extra = {}

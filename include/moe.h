@@ -105,7 +105,21 @@ typedef struct moe_params {
   int32_t router_dtype;  /* dtype of W_r (applied in fp32)                       */
   int32_t weight_dtype;  /* dtype of routed and shared expert weights            */
   int32_t accumulate;    /* moe_accumulate of the combine (MOE_ACC_F32 default)  */
+  int32_t expert_begin;  /* routed experts computed: [expert_begin, expert_end);  */
+  int32_t expert_end;    /* expert_end = 0 means n_experts (all experts)          */
 } moe_params;
+
+/* Expert range ("DeepSeek MoE.__init__: experts" and the V3 class: a rank
+ * builds only experts [experts_start_idx, experts_end_idx) and its forward
+ * loops over that range): the gate and the dispatch always cover all
+ * n_experts; moe_expert_ffn computes only the routed experts in the range
+ * (rows of other experts are left untouched), and the combine of moe_forward
+ * adds only their slots, so y is this range's share of the routed sum plus
+ * the shared output.  The routed weight stacks (w1, w3, w2 and their scales)
+ * then hold only the experts of the range: expert e is entry e - expert_begin.  A slice of the shared expert (rows of W1/W3 and the
+ * matching columns of W2, as a [dim, slice] matrix) is passed as a shared
+ * expert of width shared_inter = slice.  moe_combine itself needs the full
+ * range (it has no offsets to tell the rows apart). */
 
 /* Expert weights, device pointers.  The router weight is [E, dim] row-major.
  * The expert matrices w1, w3, w2, ws1, ws3, ws2 (logically [out, in], stacked

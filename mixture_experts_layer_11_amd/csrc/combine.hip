@@ -91,17 +91,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w,
                                                       const T* __restrict__ shared_out,
-                                                      T* __restrict__ y, int dim, int topk) {
+                                                      T* __restrict__ y, int dim, int topk,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int e_begin, int e_end) {
   const int t = blockIdx.x;
   const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (col >= dim) return;
+  // rows of the expert range (all rows without offsets)
+  const int lo = offsets != nullptr ? offsets[e_begin] : 0;
+  const int hi = offsets != nullptr ? offsets[e_end] : 0x7fffffff;
   int rs[KMAX];
   float ws[KMAX];
   sorted_slots<KMAX>(row_of + (size_t)t * topk, w + (size_t)t * topk, topk, rs, ws);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    if (j < topk) {
+    if (j < topk && rs[j] >= lo && rs[j] < hi) {
       float v[8];
       Vec8<T>::load(out + (size_t)rs[j] * dim + col, v);
 #pragma unroll
@@ -122,23 +127,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out,
 
 template <typename T, bool kLayer>
 static void launch_combine_t(dim3 grid, hipStream_t st, const void* out, const int32_t* row_of,
-                             const float* w, const void* shared_out, void* y, int dim, int topk) {
+                             const float* w, const void* shared_out, void* y, int dim, int topk,
+                             const int32_t* offsets, int eb, int ee) {
   if (topk <= 8)
     combine_kernel<T, 8, kLayer><<<grid, 256, 0, st>>>((const T*)out, row_of, w, (const T*)shared_out,
-                                                       (T*)y, dim, topk);
+                                                       (T*)y, dim, topk, offsets, eb, ee);
   else
     combine_kernel<T, kMaxTopk, kLayer><<<grid, 256, 0, st>>>((const T*)out, row_of, w,
-                                                              (const T*)shared_out, (T*)y, dim, topk);
+                                                              (const T*)shared_out, (T*)y, dim, topk,
+                                                              offsets, eb, ee);
 }
 
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
                           const void* shared_out, void* y, int ntok, int dim, int topk,
-                          bool act_f32, bool layer_acc, hipStream_t st) {
+                          bool act_f32, bool layer_acc, const int32_t* offsets, int eb, int ee,
+                          hipStream_t st) {
   dim3 grid(ntok, (dim / 8 + 255) / 256);
-  if (act_f32 && layer_acc) launch_combine_t<float, true>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
-  else if (act_f32) launch_combine_t<float, false>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
-  else if (layer_acc) launch_combine_t<uint16_t, true>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
-  else launch_combine_t<uint16_t, false>(grid, st, expert_out, row_of, topk_w, shared_out, y, dim, topk);
+  const void* o = expert_out;
+  if (act_f32 && layer_acc) launch_combine_t<float, true>(grid, st, o, row_of, topk_w, shared_out, y, dim, topk, offsets, eb, ee);
+  else if (act_f32) launch_combine_t<float, false>(grid, st, o, row_of, topk_w, shared_out, y, dim, topk, offsets, eb, ee);
+  else if (layer_acc) launch_combine_t<uint16_t, true>(grid, st, o, row_of, topk_w, shared_out, y, dim, topk, offsets, eb, ee);
+  else launch_combine_t<uint16_t, false>(grid, st, o, row_of, topk_w, shared_out, y, dim, topk, offsets, eb, ee);
   return hipGetLastError();
 }
 

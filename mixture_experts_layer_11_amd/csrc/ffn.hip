@@ -28,12 +28,13 @@ namespace moe {
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets,
                                                             int E, int ntok, int has_shared,
                                                             int bm_up, int nt_up, int nt_up_s,
-                                                            int bm_dn, int nt_dn,
+                                                            int bm_dn, int nt_dn, int e_begin,
+                                                            int e_end,
                                                             int32_t* __restrict__ sched) {
   __shared__ int su[1024], sd[1024];
   const int g = threadIdx.x;
   int cu = 0, cd = 0;
-  if (g < E) {
+  if (g < E && g >= e_begin && g < e_end) {   // experts outside the range get no tiles
     const int M = offsets[g + 1] - offsets[g];
     cu = (M + bm_up - 1) / bm_up * nt_up;
     cd = (M + bm_dn - 1) / bm_dn * nt_dn;
@@ -186,8 +187,8 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
   const int mi = min(ti.mt * 16 + r, ti.M - 1);
   const int xrow = shared ? mi : p.sorted_token[ti.row0 + mi];
   const char* bp = reinterpret_cast<const char*>(static_cast<const T*>(p.x) + (size_t)xrow * p.dim) + 16 * grp;
-  const T* W1 = shared ? static_cast<const T*>(p.ws1) : static_cast<const T*>(p.w1) + (size_t)ti.g * N * p.dim;
-  const T* W3 = shared ? static_cast<const T*>(p.ws3) : static_cast<const T*>(p.w3) + (size_t)ti.g * N * p.dim;
+  const T* W1 = shared ? static_cast<const T*>(p.ws1) : static_cast<const T*>(p.w1) + (size_t)(ti.g - p.e_begin) * N * p.dim;
+  const T* W3 = shared ? static_cast<const T*>(p.ws3) : static_cast<const T*>(p.w3) + (size_t)(ti.g - p.e_begin) * N * p.dim;
   const int rb = p.dim * (int)sizeof(T);
   const char* ap[2 * kUpNT];
 #pragma unroll
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   const T* hrow = shared ? static_cast<const T*>(p.hs) + (size_t)mi * K
                          : static_cast<const T*>(p.h) + (size_t)(ti.row0 + mi) * K;
   const char* bp = reinterpret_cast<const char*>(hrow) + 16 * grp;
-  const T* W2 = shared ? static_cast<const T*>(p.ws2) : static_cast<const T*>(p.w2) + (size_t)ti.g * N * K;
+  const T* W2 = shared ? static_cast<const T*>(p.ws2) : static_cast<const T*>(p.w2) + (size_t)(ti.g - p.e_begin) * N * K;
   const char* ap[kDnNT];
 #pragma unroll
   for (int j = 0; j < kDnNT; ++j)
@@ -425,15 +426,15 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
     wave_active = ncol0 < N;
     const int n = min(ncol0 + (fr & 15), N - 1);
     const uint16_t* W = fr < 16 ? (shared ? static_cast<const uint16_t*>(p.ws1)
-                                          : static_cast<const uint16_t*>(p.w1) + (size_t)ti.g * N * K)
+                                          : static_cast<const uint16_t*>(p.w1) + (size_t)(ti.g - p.e_begin) * N * K)
                                 : (shared ? static_cast<const uint16_t*>(p.ws3)
-                                          : static_cast<const uint16_t*>(p.w3) + (size_t)ti.g * N * K);
+                                          : static_cast<const uint16_t*>(p.w3) + (size_t)(ti.g - p.e_begin) * N * K);
     S.w = reinterpret_cast<const char*>(W) + wtile_off(n, 16 * fg, 2 * K);
   } else {
     ncol0 = ti.nt * C::BN + wave * 32;
     wave_active = ncol0 < N;
     const uint16_t* W2 = shared ? static_cast<const uint16_t*>(p.ws2)
-                                : static_cast<const uint16_t*>(p.w2) + (size_t)ti.g * N * K;
+                                : static_cast<const uint16_t*>(p.w2) + (size_t)(ti.g - p.e_begin) * N * K;
     S.w = reinterpret_cast<const char*>(W2) + wtile_off(min(ncol0 + fr, N - 1), 16 * fg, 2 * K);
   }
   // every wave runs the same instantiation: the token slices are loaded by
@@ -656,8 +657,8 @@ void stream_fp8_kernel(FfnProblem p) {
   if (kUp) {
     // A rows 0-15: W1 rows ncol0 + [0,16); rows 16-31: the same rows of W3
     ncol0 = ti.nt * F8::UPBN + wave * 16;          // N % 128 == 0: always inside
-    const size_t eoff = shared ? 0 : (size_t)ti.g * N * K;
-    const size_t soff = shared ? 0 : (size_t)ti.g * (N / 128) * KB;
+    const size_t eoff = shared ? 0 : (size_t)(ti.g - p.e_begin) * N * K;
+    const size_t soff = shared ? 0 : (size_t)(ti.g - p.e_begin) * (N / 128) * KB;
     const uint8_t* W = static_cast<const uint8_t*>(fr < 16 ? (shared ? p.ws1 : p.w1) : (shared ? p.ws3 : p.w3)) + eoff;
     S.w = reinterpret_cast<const char*>(W) + wtile_off(ncol0 + (fr & 15), 32 * fg, K);
     S.ws[0] = (shared ? p.ws1s : p.w1s) + soff + (size_t)(ncol0 / 128) * KB;
@@ -665,8 +666,8 @@ void stream_fp8_kernel(FfnProblem p) {
   } else {
     ncol0 = ti.nt * F8::BN + wave * 32;
     const int nrow = min(ncol0, N - 32);            // N % 128 == 0: a wave is all in or all out
-    const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)ti.g * N * K);
-    const float* W2s = (shared ? p.ws2s : p.w2s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nrow / 128) * KB;
+    const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)(ti.g - p.e_begin) * N * K);
+    const float* W2s = (shared ? p.ws2s : p.w2s + (size_t)(ti.g - p.e_begin) * (N / 128) * KB) + (size_t)(nrow / 128) * KB;
     S.w = reinterpret_cast<const char*>(W2) + wtile_off(nrow + fr, 32 * fg, K);
     S.ws[0] = S.ws[1] = W2s;                        // 32 rows inside one 128-row block
   }
@@ -828,10 +829,10 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   const int tok = shared ? mi : p.sorted_token[ti.row0 + mi];
   const char* bp = reinterpret_cast<const char*>(p.xq + (size_t)tok * K) + 32 * grp;
   const float* bsc = p.xs + (size_t)tok * KB;
-  const uint8_t* W1 = static_cast<const uint8_t*>(shared ? p.ws1 : p.w1) + (shared ? 0 : (size_t)ti.g * N * K);
-  const uint8_t* W3 = static_cast<const uint8_t*>(shared ? p.ws3 : p.w3) + (shared ? 0 : (size_t)ti.g * N * K);
-  const float* S1 = (shared ? p.ws1s : p.w1s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nbase / 128) * KB;
-  const float* S3 = (shared ? p.ws3s : p.w3s + (size_t)ti.g * (N / 128) * KB) + (size_t)(nbase / 128) * KB;
+  const uint8_t* W1 = static_cast<const uint8_t*>(shared ? p.ws1 : p.w1) + (shared ? 0 : (size_t)(ti.g - p.e_begin) * N * K);
+  const uint8_t* W3 = static_cast<const uint8_t*>(shared ? p.ws3 : p.w3) + (shared ? 0 : (size_t)(ti.g - p.e_begin) * N * K);
+  const float* S1 = (shared ? p.ws1s : p.w1s + (size_t)(ti.g - p.e_begin) * (N / 128) * KB) + (size_t)(nbase / 128) * KB;
+  const float* S3 = (shared ? p.ws3s : p.w3s + (size_t)(ti.g - p.e_begin) * (N / 128) * KB) + (size_t)(nbase / 128) * KB;
   const char* ap[4];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -916,8 +917,8 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   const size_t hrow = shared ? (size_t)mi : (size_t)(ti.row0 + mi);
   const char* bp = reinterpret_cast<const char*>(static_cast<const uint8_t*>(shared ? p.hs : p.h) + hrow * K) + 32 * grp;
   const float* bsc = (shared ? p.hsscale : p.hscale) + hrow * KB;
-  const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)ti.g * N * K);
-  const float* S2 = (shared ? p.ws2s : p.w2s + (size_t)ti.g * (N / 128) * KB);
+  const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)(ti.g - p.e_begin) * N * K);
+  const float* S2 = (shared ? p.ws2s : p.w2s + (size_t)(ti.g - p.e_begin) * (N / 128) * KB);
   const char* ap[kDnNT];
   const float* sp[kDnNT];
 #pragma unroll
@@ -1013,7 +1014,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const int nt_up = ceil_div(p.inter, bn_up), nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
   const int nt_dn = ceil_div(p.dim, bn_dn);
   ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.offsets, p.E, p.ntok, has_shared ? 1 : 0, bm, nt_up,
-                                          nt_up_s, bm, nt_dn, p.sched);
+                                          nt_up_s, bm, nt_dn, p.e_begin, p.e_end, p.sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   FfnProblem q = p;

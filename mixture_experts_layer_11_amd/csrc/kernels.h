@@ -47,6 +47,7 @@ struct FfnProblem {
   void* shared_out;            // shared outputs [T, dim] act dtype (NULL = skip)
   int32_t* sched;              // scratch, 2 * (E + 2) ints
   int ntok, dim, E, topk, inter, inter_s;
+  int e_begin, e_end;          // routed experts computed: [e_begin, e_end)
   bool act_f32;
   WKind wkind;
   hipEvent_t ev[4];            // optional timing: up start/end, down start/end (or null)
@@ -64,8 +65,11 @@ hipError_t launch_pack_weights(const uint8_t* src, int64_t rows, int64_t row_byt
 // combine.hip
 // layer_acc: accumulate in the layer dtype over the experts in ascending id
 // (rows ascend with the expert id), casting after every addition.
+// offsets (may be NULL for all experts): only rows [offsets[e_begin],
+// offsets[e_end]) - the experts of the range - are added.
 hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
                           const void* shared_out, void* y, int ntok, int dim, int topk,
-                          bool act_f32, bool layer_acc, hipStream_t st);
+                          bool act_f32, bool layer_acc, const int32_t* offsets, int e_begin,
+                          int e_end, hipStream_t st);
 
 }  // namespace moe

@@ -46,6 +46,9 @@ void profile_slot(hipEvent_t (&ev)[4]) {
 
 size_t align_up(size_t n) { return (n + 255) & ~size_t(255); }
 
+int expert_end(const moe_params* p) { return p->expert_end == 0 ? p->n_experts : p->expert_end; }
+bool full_range(const moe_params* p) { return p->expert_begin == 0 && expert_end(p) == p->n_experts; }
+
 // Workspace carve-up (offsets in bytes, each 256-byte aligned).
 struct Layout {
   size_t logits, rpart, topk_idx, topk_w, counts, offsets, sorted_token, row_of, perm, sched;
@@ -108,6 +111,9 @@ moe_status validate(const moe_params* p, int64_t T) {
     return fail(MOE_ERR_INVALID_ARG, "unknown score_func");
   if (p->accumulate != MOE_ACC_F32 && p->accumulate != MOE_ACC_LAYER)
     return fail(MOE_ERR_INVALID_ARG, "unknown accumulate mode");
+  const int eend = p->expert_end == 0 ? E : p->expert_end;
+  if (p->expert_begin < 0 || p->expert_begin > eend || eend > E)
+    return fail(MOE_ERR_INVALID_ARG, "expert range must satisfy 0 <= expert_begin <= expert_end <= n_experts");
   if (p->dim < 1 || p->inter < 1 || p->shared_inter < 0)
     return fail(MOE_ERR_INVALID_ARG, "dim and inter must be >= 1, shared_inter >= 0");
   const bool f32 = p->act_dtype == MOE_F32 && p->router_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
@@ -184,6 +190,7 @@ moe_status do_ffn(const moe_params* p, int64_t T, const void* x, const int32_t* 
   f.sched = at<int32_t>(ws, L.sched);
   f.ntok = (int)T; f.dim = p->dim; f.E = p->n_experts; f.topk = p->topk;
   f.inter = p->inter; f.inter_s = p->shared_inter;
+  f.e_begin = p->expert_begin; f.e_end = expert_end(p);
   f.act_f32 = p->act_dtype == MOE_F32;
   f.wkind = wkind(p);
   profile_slot(f.ev);
@@ -331,9 +338,11 @@ moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
   if (s != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!expert_out || !row_of || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!full_range(p)) return fail(MOE_ERR_UNSUPPORTED, "moe_combine needs the full expert range");
   hipError_t e = moe::launch_combine(expert_out, row_of, topk_w, shared_out, y, (int)T, p->dim,
                                      p->topk, p->act_dtype == MOE_F32,
-                                     p->accumulate == MOE_ACC_LAYER, (hipStream_t)stream);
+                                     p->accumulate == MOE_ACC_LAYER, nullptr, 0, p->n_experts,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 
@@ -388,7 +397,8 @@ moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_
   if ((s = do_permute(p, T, idx, cnt, off, st_tok, row_of, workspace, st)) != MOE_OK) return s;
   if ((s = do_ffn(p, T, x, st_tok, off, w, out, sh, workspace, st)) != MOE_OK) return s;
   hipError_t e = moe::launch_combine(out, row_of, wt, sh, y, (int)T, p->dim, p->topk,
-                                     p->act_dtype == MOE_F32, p->accumulate == MOE_ACC_LAYER, st);
+                                     p->act_dtype == MOE_F32, p->accumulate == MOE_ACC_LAYER,
+                                     full_range(p) ? nullptr : off, p->expert_begin, expert_end(p), st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
 }
 

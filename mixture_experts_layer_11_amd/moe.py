@@ -38,7 +38,8 @@ class moe_params(ctypes.Structure):
                 ("shared_inter", ctypes.c_int32), ("score_func", ctypes.c_int32),
                 ("route_scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
                 ("router_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("accumulate", ctypes.c_int32)]
+                ("accumulate", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
+                ("expert_end", ctypes.c_int32)]
 
 
 _VP = ctypes.c_void_p
@@ -128,6 +129,8 @@ class Params:
     router_dtype: str
     weight_dtype: str
     accumulate: str = "f32"   # "f32" or "layer" (moe_accumulate)
+    expert_begin: int = 0     # routed experts computed: [expert_begin, expert_end)
+    expert_end: int = 0       # 0 = n_experts
 
     @staticmethod
     def from_config(cfg) -> "Params":
@@ -139,7 +142,8 @@ class Params:
         return moe_params(self.dim, self.n_experts, self.n_groups, self.topk_groups, self.topk,
                           self.inter, self.shared_inter, _SCORE[self.score_func],
                           self.route_scale, _DT[self.act_dtype], _DT[self.router_dtype],
-                          _DT[self.weight_dtype], _ACC[self.accumulate])
+                          _DT[self.weight_dtype], _ACC[self.accumulate], self.expert_begin,
+                          self.expert_end)
 
     @property
     def act_torch(self):
@@ -286,25 +290,30 @@ def to_device(a, dtype_tag: str, device="cuda") -> torch.Tensor:
     return t.to(device)
 
 
-def upload_layer(layer, device="cuda") -> DeviceWeights:
+def upload_layer(layer, device="cuda", experts=None) -> DeviceWeights:
     """Copy a drawn layer's weights (storage format) to the device; the expert
-    matrices are rewritten into the tiled layout (moe_pack_weights)."""
+    matrices are rewritten into the tiled layout (moe_pack_weights).
+    experts=(b, e): only the routed experts b..e-1 are uploaded (an expert
+    range, see Params.expert_begin / expert_end)."""
     cfg = layer.cfg
     wd = cfg.w_dtype
-    f32 = lambda a: None if a is None else to_device(a, "f32", device)
+    sl = slice(None) if experts is None else slice(experts[0], experts[1])
+    f32 = lambda a: None if a is None else to_device(a[sl] if a.ndim == 3 else a, "f32", device)
 
     def mat(a):
         t = to_device(a, wd, device)
         packed = moe_pack_weights(t)
         del t
         return packed
-    dw = DeviceWeights(to_device(layer.wr, cfg.router_dtype, device), f32(layer.bias),
-                       mat(layer.w1), mat(layer.w3), mat(layer.w2), f32(layer.w1_s),
+    bias = None if layer.bias is None else to_device(layer.bias, "f32", device)
+    dw = DeviceWeights(to_device(layer.wr, cfg.router_dtype, device), bias,
+                       mat(layer.w1[sl]), mat(layer.w3[sl]), mat(layer.w2[sl]), f32(layer.w1_s),
                        f32(layer.w3_s), f32(layer.w2_s))
     if layer.shared is not None:
         s = layer.shared
         dw.ws1, dw.ws3, dw.ws2 = mat(s.w1), mat(s.w3), mat(s.w2)
-        dw.ws1_scale, dw.ws3_scale, dw.ws2_scale = f32(s.w1_s), f32(s.w3_s), f32(s.w2_s)
+        g = lambda a: None if a is None else to_device(a, "f32", device)
+        dw.ws1_scale, dw.ws3_scale, dw.ws2_scale = g(s.w1_s), g(s.w3_s), g(s.w2_s)
     return dw
 
 

@@ -380,12 +380,15 @@ def expert_ffn(xv: np.ndarray, w1, w3, w2, w_dtype: str, act_dtype: str,
 # ---------------------------------------------------------------------------
 
 
-def combine(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out=None) -> np.ndarray:
+def combine(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out=None,
+            experts=None) -> np.ndarray:
     """fp32 accumulator y = 0; for each expert in ascending id, y[t] += out[t,k] * w[t,k]
     (product then sum, each rounded to fp32); then y += shared output.
 
     outs [T, topk, dim]: each assignment's expert output (layer-dtype values);
     w [T, topk] fp32; idx [T, topk]; shared_out [T, dim] or None.
+    experts: optional (b, e) - only experts b..e-1 contribute ([v3]: a rank's
+    forward loops over its own experts only).
     Returns the fp32 accumulator (cast it with round_to).
     """
     T, K, dim = outs.shape
@@ -395,14 +398,19 @@ def combine(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out=None) -
         k = order[:, j]
         o = outs[np.arange(T), k].astype(F32)
         contrib = (o * w[np.arange(T), k][:, None].astype(F32)).astype(F32)
-        y = (y + contrib).astype(F32)
+        if experts is None:
+            y = (y + contrib).astype(F32)
+        else:
+            e = idx[np.arange(T), k]
+            keep = ((e >= experts[0]) & (e < experts[1]))[:, None]
+            y = np.where(keep, (y + contrib).astype(F32), y)
     if shared_out is not None:
         y = (y + np.asarray(shared_out).astype(F32)).astype(F32)
     return y
 
 
 def combine_layer(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out,
-                  act_dtype: str) -> np.ndarray:
+                  act_dtype: str, experts=None) -> np.ndarray:
     """[v3] MoE.forward with y held in the layer dtype (R9): y = 0; for each
     expert in ascending id, y[t] = cast(y[t] + out[t,k] * w[t,k]) where the
     product and the sum are fp32 and cast rounds to the layer dtype; then
@@ -418,7 +426,12 @@ def combine_layer(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out,
         k = order[:, j]
         o = outs[np.arange(T), k].astype(F32)
         contrib = (o * w[np.arange(T), k][:, None].astype(F32)).astype(F32)
-        y = round_to((y + contrib).astype(F32), act_dtype).astype(F32)
+        upd = round_to((y + contrib).astype(F32), act_dtype).astype(F32)
+        if experts is None:
+            y = upd
+        else:
+            e = idx[np.arange(T), k]
+            y = np.where(((e >= experts[0]) & (e < experts[1]))[:, None], upd, y)
     if shared_out is not None:
         y = round_to((y + np.asarray(shared_out).astype(F32)).astype(F32), act_dtype).astype(F32)
     return y.astype(np.float64)
@@ -426,7 +439,7 @@ def combine_layer(outs: np.ndarray, w: np.ndarray, idx: np.ndarray, shared_out,
 
 def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_dtype,
                 router_dtype, E, n_groups, topk_groups, topk, score_func, route_scale,
-                tokens=None, route=None, accumulate="f32"):
+                tokens=None, route=None, accumulate="f32", experts=None):
     """y = cast( sum_k w[t,k] * FFN_{idx[t,k]}(x_t) + FFN_shared(x_t) ).
 
     x, wr: storage-format arrays; expert_weights(e) -> (w1, w3, w2, w1_s, w3_s,
@@ -434,7 +447,9 @@ def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_d
     ids (the gate still runs on exactly those rows: routing is per token).
     route: optional (weights, idx) to use instead of the gate's own (for tokens
     whose top-k is undecided within the margin).  accumulate: "f32" ([combine])
-    or "layer" ([v3], R9).
+    or "layer" ([v3], R9).  experts: optional (b, e), the routed experts that
+    contribute ([v3] constructor and forward: a rank holds and loops over
+    experts_start_idx..experts_end_idx-1); the gate still sees all experts.
 
     Returns dict(y=[n, dim] fp64 values of the cast output, y32=fp32
     accumulator (None in the layer mode), w, idx, info).
@@ -450,7 +465,8 @@ def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_d
         info = {}
     xq = quantize_act_1x128(xv)[2] if w_dtype == "fp8" else None
     outs = np.zeros(idx.shape + (xv.shape[1],))             # FFN_{idx[t,k]}(x_t)
-    for e in range(E):                                      # ascending expert order
+    lo, hi = (0, E) if experts is None else experts
+    for e in range(lo, hi):                                 # ascending expert order
         rows, slots = np.nonzero(idx == e)
         if rows.size == 0:
             continue
@@ -462,11 +478,11 @@ def moe_forward(x, wr, bias, expert_weights: Callable, shared, *, act_dtype, w_d
         w1, w3, w2, s1, s3, s2 = shared
         sh = expert_ffn(xv, w1, w3, w2, w_dtype, act_dtype, s1, s3, s2, xq)
     if accumulate == "layer":
-        return {"y": combine_layer(outs, w, idx, sh, act_dtype), "y32": None, "w": w,
+        return {"y": combine_layer(outs, w, idx, sh, act_dtype, experts), "y32": None, "w": w,
                 "idx": idx, "info": info, "tokens": tok}
     if accumulate != "f32":
         raise ValueError(accumulate)
-    y = combine(outs, w, idx, sh)
+    y = combine(outs, w, idx, sh, experts)
     return {"y": round_to(y.astype(np.float64), act_dtype), "y32": y, "w": w, "idx": idx,
             "info": info, "tokens": tok}
 

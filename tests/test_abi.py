@@ -83,6 +83,23 @@ def test_unknown_accumulate_mode_rejected():
     assert moe.lib().moe_workspace_size(ctypes.byref(pc), 16, ctypes.byref(n)) == moe.MOE_OK
 
 
+@pytest.mark.parametrize("b,e,status", [(0, 0, 0), (0, 256, 0), (32, 64, 0), (5, 5, 0),
+                                         (-1, 8, 1), (9, 8, 1), (0, 257, 1)])
+def test_expert_range_validation(b, e, status):
+    pc = _p().c()
+    pc.expert_begin, pc.expert_end = b, e
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_workspace_size(ctypes.byref(pc), 16, ctypes.byref(n)) == status
+
+
+def test_combine_needs_full_expert_range():
+    pc = _p().c()
+    pc.expert_begin, pc.expert_end = 0, 32
+    fake = ctypes.c_void_p(256)
+    s = moe.lib().moe_combine(ctypes.byref(pc), 16, fake, fake, fake, None, fake, None)
+    assert s == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_workspace_size_grows_with_T_and_is_aligned():
     p = _p()
     s1, n1 = _ws_status(p, 16)

@@ -291,6 +291,28 @@ def test_forward_parity_layer_accumulator(ci, layers):
     assert same.mean() > 0.97
 
 
+@pytest.mark.parametrize("ci,rng_", [(1, (8, 24)), (0, (0, 4)), (3, (7, 16)), (9, (2, 5))])
+def test_forward_parity_expert_range(ci, rng_):
+    # one rank's share: only experts b..e-1 are uploaded and computed
+    cfg = inputs.SMALL_CONFIGS[ci]
+    layer = inputs.draw_layer(cfg)
+    dw = moe.upload_layer(layer, experts=rng_)
+    p = moe.Params.from_config(cfg)
+    p.expert_begin, p.expert_end = rng_
+    ws = moe.alloc_workspace(p, cfg.T)
+    g_idx = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device=DEV)
+    g_w = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device=DEV)
+    y = moe.moe_forward(p, _x_dev(layer), dw, ws, topk_idx=g_idx, topk_w=g_w)
+    _sync()
+    r = oracle.moe_forward(layer.x, layer.wr, layer.bias, expert_fn(layer), shared_tuple(layer),
+                           experts=rng_, **oracle_kwargs(cfg))
+    same = check_routing(cfg, r["w"], r["idx"], r["info"], g_idx.cpu().numpy(),
+                         g_w.cpu().numpy(), layer.bias)
+    mx, mean = rel_errors(moe.to_host_values(y)[same], r["y"][same])
+    assert mx <= bar(cfg)[0] and mean <= bar(cfg)[1], (mx, mean)
+    assert same.mean() > 0.97
+
+
 def test_forward_deterministic(layers):
     cfg = inputs.SMALL_CONFIGS[1]
     layer, dw = layers(cfg)

@@ -413,3 +413,28 @@ def test_combine_layer_differs_from_fp32_accumulator_within_rounding():
     scale = np.abs(outs).sum(1).max(-1, keepdims=True) + np.abs(sh).max(-1, keepdims=True)
     assert np.all(np.abs(a - b) <= (K + 2) * 2.0 ** -8 * scale)
     assert np.any(a != b)          # and they are different methods
+
+
+# ---------------------------------------------------------------------------
+# expert ranges ([v3] constructor and forward: a rank's experts only)
+# ---------------------------------------------------------------------------
+
+def test_expert_ranges_partition_the_routed_sum():
+    from tests.helpers import expert_fn, oracle_kwargs
+    layer = inputs.draw_layer(tiny_cfg("ranges", T=40, E=16, n_groups=4, topk_groups=2, topk=4))
+    kw = oracle_kwargs(layer.cfg)
+    full = oracle.moe_forward(layer.x, layer.wr, layer.bias, expert_fn(layer), None, **kw)
+    same = oracle.moe_forward(layer.x, layer.wr, layer.bias, expert_fn(layer), None,
+                              experts=(0, 16), **kw)
+    np.testing.assert_array_equal(full["y32"], same["y32"])
+    parts = [oracle.moe_forward(layer.x, layer.wr, layer.bias, expert_fn(layer), None,
+                                experts=(b, b + 4), **kw)["y32"].astype(np.float64)
+             for b in range(0, 16, 4)]
+    total = np.sum(parts, axis=0)
+    # the same terms summed in another grouping: equal up to fp32 rounding
+    scale = np.abs(full["y32"]).max()
+    assert np.abs(total - full["y32"]).max() <= 1e-5 * scale
+    # each part only holds its experts' terms
+    empty = oracle.moe_forward(layer.x, layer.wr, layer.bias, expert_fn(layer), None,
+                               experts=(5, 5), **kw)
+    assert not np.any(empty["y32"])
