@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--experts", default="",
                     help="b:e - time one expert-parallel rank's share: only routed experts b..e-1 "
                          "(their weights alone are uploaded); the gate still covers all experts")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one forward in a HIP graph and time its replays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -113,7 +115,8 @@ def traffic_for(kernel, workload):
     return ent["hbm_bytes_per_launch"]
 
 
-def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False, experts=None):
+def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False, experts=None,
+               graph=False):
     layer = inputs.draw_layer(cfg)
     dw = moe.upload_layer(layer, experts=experts)
     p = moe.Params.from_config(cfg)
@@ -127,16 +130,31 @@ def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False, experts
     for _ in range(warmup):
         moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
     torch.cuda.synchronize()
-    moe.moe_profile_start(steps)
+    step = lambda: moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
+        torch.cuda.synchronize()
+        step = g.replay
+    if not graph:
+        moe.moe_profile_start(steps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     wall0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
+        step()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if graph:
+        # the per-kernel events are host-side records, absent from a replay:
+        # time the expert kernels over the same number of eager calls
+        moe.moe_profile_start(steps)
+        for _ in range(steps):
+            moe.moe_forward(p, x, dw, ws, y=y, counts=counts)
+        torch.cuda.synchronize()
     ncalls, up_ms, dn_ms = moe.moe_profile_stop()
     ms = ev[0].elapsed_time(ev[steps]) / steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
@@ -207,7 +225,7 @@ def main():
     cfg = inputs.config_by_name(a.config)
     experts = tuple(int(v) for v in a.experts.split(":")) if a.experts else None
     res, layer = run_config(cfg, a.steps, a.warmup, torch, moe, inputs, want_layer=True,
-                            experts=experts)
+                            experts=experts, graph=a.graph)
     tok_s = cfg.T / (res["ms"] / 1e3)
     up_gbs = res["up_bytes"] / (res["up_ms"] / 1e3) / 1e9
     traffic = None if experts else traffic_for("up_grouped_gemm", cfg.name)
@@ -222,6 +240,7 @@ def main():
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(res["ms"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dt, "data": "synthetic (seeded; random-init weights of the layer shape)",
+        "launch": "hip_graph" if a.graph else "eager",
         "config": {"workload": cfg.name, "T": cfg.T, "dim": cfg.dim, "n_experts": cfg.E,
                    "topk": cfg.topk, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
                    "inter": cfg.inter, "shared_inter": cfg.inter_shared,
@@ -238,7 +257,7 @@ def main():
     extra = {}
     for name in [s for s in a.also.split(",") if s]:
         c2 = inputs.config_by_name(name)
-        r2, _ = run_config(c2, max(5, a.steps // 2), a.warmup, torch, moe, inputs)
+        r2, _ = run_config(c2, max(5, a.steps // 2), a.warmup, torch, moe, inputs, graph=a.graph)
         extra[c2.name] = {
             "tokens_per_s": round(c2.T / (r2["ms"] / 1e3), 1), "ms_per_step": round(r2["ms"], 4),
             "ms_median": round(r2["ms_median"], 4), "ms_min": round(r2["ms_min"], 4),

@@ -344,3 +344,35 @@ EDGE_CFGS = [
 def test_forward_edge_cases(cfg, layers):
     layer, dw = layers(cfg)
     forward_and_check(cfg, layer, dw)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: the whole forward enqueues no allocation, memset or host
+# synchronisation, so it can be captured once and replayed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ci", [1, 3])
+def test_forward_graph_replays_match_eager(ci, layers):
+    cfg = inputs.SMALL_CONFIGS[ci]
+    layer, dw = layers(cfg)
+    p = moe.Params.from_config(cfg)
+    ws = moe.alloc_workspace(p, cfg.T)
+    x = _x_dev(layer)
+    y = torch.empty((cfg.T, cfg.dim), dtype=p.act_torch, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # warm-up outside the capture
+        moe.moe_forward(p, x, dw, ws, y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(p, x, dw, ws, y=y)
+    for _ in range(3):
+        y.fill_(0)                                     # eager work between replays
+        ws.fill_(0x3C)
+        _sync()
+        g.replay()
+        _sync()
+        assert torch.equal(y.view(torch.int16), eager.view(torch.int16))
