@@ -47,6 +47,8 @@ def parse():
                          "(their weights alone are uploaded); the gate still covers all experts")
     ap.add_argument("--graph", action="store_true",
                     help="capture one forward in a HIP graph and time its replays")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured ceilings (streaming read, dense bf16 GEMM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -169,6 +171,46 @@ def run_config(cfg, steps, warmup, torch, moe, inputs, want_layer=False, experts
     return res, layer
 
 
+def measured_peaks(torch, moe):
+    """What the machine delivers, beside the published peaks: the library's
+    streaming-read kernel over a 4 GiB buffer (every byte once), and a dense
+    8192^3 bf16 GEMM through torch.matmul (hipBLASLt).  Best of 5 runs each."""
+    stream = torch.cuda.current_stream()
+
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            out.append(a.elapsed_time(b))
+        return min(out)
+
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    read_ms = best_ms(lambda: moe.moe_stream_read(buf, sink))
+    del buf
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    gemm_ms = best_ms(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBs": round(nbytes / (read_ms / 1e3) / 1e9, 1),
+            "hbm_read_frac_of_peak": round(nbytes / (read_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bf16_gemm_TFLOPs": round(2 * n ** 3 / (gemm_ms / 1e3) / 1e12, 1),
+            "bf16_gemm_frac_of_peak": round(2 * n ** 3 / (gemm_ms / 1e3) / 1e12
+                                            / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "how": "moe_stream_read over 4 GiB; torch.matmul 8192^3 bf16; best of 5"}
+
+
 def floors(cfg, res):
     """Roofline floor of one forward: max(algorithmic FLOPs / MFMA peak,
     algorithmic bytes / HBM peak), and which one binds."""
@@ -222,6 +264,7 @@ def main():
         return
     from mixture_experts_layer_11_amd import inputs, moe
     moe.lib()
+    peaks = None if a.no_peaks else measured_peaks(torch, moe)
     cfg = inputs.config_by_name(a.config)
     experts = tuple(int(v) for v in a.experts.split(":")) if a.experts else None
     res, layer = run_config(cfg, a.steps, a.warmup, torch, moe, inputs, want_layer=True,
@@ -267,6 +310,8 @@ def main():
         }
     if extra:
         out["also"] = extra
+    if peaks:
+        out["measured_peaks"] = peaks
     print(json.dumps(out), flush=True)
 
 

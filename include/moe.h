@@ -250,6 +250,16 @@ moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_
 moe_status moe_profile_start(int32_t max_calls);
 moe_status moe_profile_stop(int32_t* calls, float* up_ms, float* down_ms);
 
+/* Measurement helper (not part of the layer): enqueue one kernel that reads
+ * every byte of buf once, 16-byte coalesced loads, 8 per lane in flight, 8
+ * workgroups of 256 threads per CU.  Timing it gives the HBM read rate this
+ * library's kernels can reach on the machine, to set beside the published
+ * peak.  buf: device, bytes a positive multiple of 16; sink: one device
+ * uint32, written only in a case that does not arise for zero-filled buffers.
+ * MOE_ERR_INVALID_ARG on NULL pointers or a bad size, MOE_ERR_HIP if the
+ * launch fails. */
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Readable name of a status; never NULL. */
 const char* moe_status_string(moe_status s);
 

@@ -1,0 +1,49 @@
+// Streaming-read kernel for measurement: the HBM read rate one kernel of this
+// library can reach on the machine, the practical ceiling beside the 8 TB/s
+// published peak.  Not part of the layer.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;   // 16-byte loads in flight per lane
+
+// Every 16-byte word of buf is read exactly once: workgroup b reads chunks
+// b, b + grid, ... of kThreads * kUnroll words, coalesced per load.  The XOR
+// of all words goes to sink only if it equals an arbitrary constant, which
+// keeps the loads live without a store per thread.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ buf,
+                                                               size_t nvec,
+                                                               uint32_t* __restrict__ sink) {
+  const size_t chunk = (size_t)kThreads * kUnroll;
+  uint32_t acc = 0;
+  for (size_t base = (size_t)blockIdx.x * chunk + threadIdx.x; base < nvec;
+       base += (size_t)gridDim.x * chunk) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      v[u] = i < nvec ? buf[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+}  // namespace
+
+namespace moe {
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const size_t nvec = bytes / 16;
+  const size_t chunk = (size_t)kThreads * kUnroll;
+  const size_t chunks = (nvec + chunk - 1) / chunk;
+  const unsigned grid = (unsigned)(chunks < 2048 ? chunks : 2048);   // 8 workgroups per CU
+  stream_read_kernel<<<grid, kThreads, 0, st>>>((const uint4*)buf, nvec, sink);
+  return hipGetLastError();
+}
+
+}  // namespace moe

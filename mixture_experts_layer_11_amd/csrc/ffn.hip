@@ -70,6 +70,8 @@ struct TileInfo {
   int row0;     // first row of the group in the expert-contiguous order
   int M;        // rows of the group
   int mt, nt;   // tile coordinates
+  int m0;       // first row of the m-tile within the group
+  int mrows;    // rows of the m-tile (> 0)
 };
 
 // Maps this workgroup to a tile; returns false when it has none.  The grid is
@@ -77,7 +79,11 @@ struct TileInfo {
 // device), so the XCD-aware remap runs over the real count rounded up to 8:
 // every XCD then gets an equal, contiguous range of tiles (all n-tiles and
 // m-tiles of an expert next to each other, sharing its rows in that XCD's
-// L2), and the surplus workgroups exit.
+// L2), and the surplus workgroups exit.  A group of M rows is cut into
+// ceil(M / bm) m-tiles of equal size (rounded up to the 32-row sub-tile, or to
+// bm when bm < 32), the last one taking the remainder: m-tiles of one expert
+// then take about the same time and stream its weight slices together, so the
+// second reads them from L2.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ sched,
                                           const int32_t* __restrict__ offsets, int E, int ntok,
                                           int bm, TileInfo& ti) {
@@ -98,6 +104,10 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ sched,
   const int local = tile - sched[lo];
   ti.mt = local % mtiles;
   ti.nt = local / mtiles;
+  const int gran = bm < 32 ? bm : 32;
+  const int per = min(bm, ((ti.M + mtiles - 1) / mtiles + gran - 1) / gran * gran);
+  ti.m0 = ti.mt * per;                 // (mtiles - 1) * per < M: every m-tile has rows
+  ti.mrows = min(per, ti.M - ti.m0);
   return true;
 }
 
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
   const int r = lane & 15, grp = lane >> 4;
   const int nbase = ti.nt * kUpBN + wave * 16 * kUpNT;
   if (nbase >= N) return;
-  const int mi = min(ti.mt * 16 + r, ti.M - 1);
+  const int mi = ti.m0 + min(r, ti.mrows - 1);
   const int xrow = shared ? mi : p.sorted_token[ti.row0 + mi];
   const char* bp = reinterpret_cast<const char*>(static_cast<const T*>(p.x) + (size_t)xrow * p.dim) + 16 * grp;
   const T* W1 = shared ? static_cast<const T*>(p.ws1) : static_cast<const T*>(p.w1) + (size_t)(ti.g - p.e_begin) * N * p.dim;
@@ -202,8 +212,8 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
   for (int j = 0; j < 2 * kUpNT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   kloop<T, 2 * kUpNT, 2>(ap, bp, p.dim * (int)sizeof(T) / 64, acc);
 
-  const int m = ti.mt * 16 + r;
-  if (m < ti.M) {
+  const int m = ti.m0 + r;
+  if (r < ti.mrows) {
     T* hrow = shared ? static_cast<T*>(p.hs) + (size_t)m * N
                      : static_cast<T*>(p.h) + (size_t)(ti.row0 + m) * N;
 #pragma unroll
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   const int r = lane & 15, grp = lane >> 4;
   const int nbase = ti.nt * kDnBN + wave * 16 * kDnNT;
   if (nbase >= N) return;
-  const int mi = min(ti.mt * 16 + r, ti.M - 1);
+  const int mi = ti.m0 + min(r, ti.mrows - 1);
   const T* hrow = shared ? static_cast<const T*>(p.hs) + (size_t)mi * K
                          : static_cast<const T*>(p.h) + (size_t)(ti.row0 + mi) * K;
   const char* bp = reinterpret_cast<const char*>(hrow) + 16 * grp;
@@ -243,8 +253,8 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   for (int j = 0; j < kDnNT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   kloop<T, kDnNT, 2>(ap, bp, K * (int)sizeof(T) / 64, acc);
 
-  const int m = ti.mt * 16 + r;
-  if (m < ti.M) {
+  const int m = ti.m0 + r;
+  if (r < ti.mrows) {
     T* orow = shared ? static_cast<T*>(p.shared_out) + (size_t)m * N
                      : static_cast<T*>(p.out) + (size_t)(ti.row0 + m) * N;
 #pragma unroll
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 // ---------------------------------------------------------------------------
 // Tile shape of the stream kernel: BM token rows, WAVES waves of 32 weight
 // rows each, 64-element K slices.
-template <int BM_, int WAVES_, int RING_, int XD_ = 2>
+template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4>
 struct SCfg {
   static constexpr int BM = BM_;
   static constexpr int WAVES = WAVES_;
@@ -295,8 +305,11 @@ struct SCfg {
   static constexpr int ROWS_PER_PASS = THREADS / TPR;
   static constexpr int XLOADS = (BM + ROWS_PER_PASS - 1) / ROWS_PER_PASS;
   static constexpr int RING = RING_;               // weight register stages (RING-1 slices ahead)
-  static constexpr int XD = XD_;                   // token register stages (XD slices ahead)
-  static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), 2);   // steps with compile-time stage indices
+  static constexpr int XD = XD_;                   // token register stages
+  static constexpr int NB = NB_;                   // token LDS buffers
+  static constexpr int D = NB / 2;                 // steps per barrier; slice kt+D is stored after step kt
+  static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), D);   // steps with compile-time stage indices
+  static_assert(NB == 2 || NB == 4, "two or four token buffers");
 };
 using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
 using SHuge = SCfg<256, 8, 2, 2>; // experts of many hundred tokens: larger tiles, shallower rings
@@ -316,13 +329,13 @@ __device__ __forceinline__ f32x16_t mma32(f32x16_t c, uint4 a, uint4 b) {
 }
 
 template <class C, int MT>
-__device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const StreamSrc<C>& S, int nk,
+__device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const StreamSrc<C>& S, int nk,
                                              f32x16_t (&acc)[C::MT]) {
   const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
   uint4 wr[C::RING][C::KS];   // weight slices in flight: [slice % RING][k-step]
   // token load passes that reach the MT*32 rows this instantiation reads
   constexpr int XL = std::min(C::XLOADS, (32 * MT + C::ROWS_PER_PASS - 1) / C::ROWS_PER_PASS);
-  uint4 xr[C::XD][C::XLOADS]; // token slices kt+1 .. kt+XD in flight: [slice % XD]
+  uint4 xr[C::XD][C::XLOADS]; // token slices in flight between load and LDS store: [slice % XD]
   auto wload = [&](uint4 (&dst)[C::KS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
@@ -339,22 +352,32 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const Stream
     for (int i = 0; i < XL; ++i)
       if (S.xact[i]) *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + C::ROWS_PER_PASS * i * C::STRIDE]) = src[i];
   };
+  // token slice j lives in LDS buffer j % NB.  Slices 0 .. D-1 go to LDS
+  // first; slices D .. D+XD-2 wait in registers.
 #pragma unroll
-  for (int j = 0; j < C::XD; ++j) xload(xr[j], j);
+  for (int j = 0; j < C::D; ++j) {
+    xload(xr[j % C::XD], j);
+    xstore(xr[j % C::XD], j);
+  }
+#pragma unroll
+  for (int j = C::D; j < C::D + C::XD - 1; ++j) xload(xr[j % C::XD], j);
 #pragma unroll
   for (int j = 0; j < C::RING - 1; ++j) wload(wr[j], j);
-  xstore(xr[0], 0);
   __syncthreads();
-  // step kt (R = kt % UNROLL, compile-time): issue token slice kt+XD, then
-  // weight slice kt+RING-1; compute slice kt; store token slice kt+1 (issued
-  // XD-1 steps earlier), so the newer slices stay in flight across the barrier.
+  // step kt (R = kt % UNROLL, compile-time): issue token slice kt+D-1+XD,
+  // then weight slice kt+RING-1; compute slice kt; store token slice kt+D
+  // (issued XD-1 steps earlier) into the buffer slice kt+D-NB left, so the
+  // newer slices stay in flight across the barrier.  One barrier every D
+  // steps: it orders the stores of the D slices before it against their
+  // reads D steps later, and the reads of the D slices before it against
+  // the stores that reuse their buffers.
   auto step = [&](int kt, auto R) {
     constexpr int r = decltype(R)::value;
     constexpr int ws = r % C::RING;
-    xload(xr[r % C::XD], kt + C::XD);
+    xload(xr[(r + C::D - 1 + C::XD) % C::XD], kt + C::D - 1 + C::XD);
     wload(wr[(ws + C::RING - 1) % C::RING], kt + C::RING - 1);
     __builtin_amdgcn_sched_barrier(0);
-    const char* sb = sx[r & 1] + fr * C::STRIDE + 16 * fg;
+    const char* sb = sx[kt % C::NB] + fr * C::STRIDE + 16 * fg;
     // fragments of k-step s+1 are read from LDS while k-step s is multiplied
     uint4 fx[2][MT];
 #pragma unroll
@@ -371,8 +394,8 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const Stream
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       }
     }
-    xstore(xr[(r + 1) % C::XD], (r + 1) & 1);
-    __syncthreads();
+    xstore(xr[(r + C::D) % C::XD], (kt + C::D) % C::NB);
+    if (r % C::D == C::D - 1) __syncthreads();
   };
   auto body = [&](int kt0, auto... R) { (step(kt0 + decltype(R)::value, R), ...); };
   auto tail = [&](int kt0, auto... R) {
@@ -387,7 +410,7 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[2][C::LDS], const Stream
 }
 
 template <class C, bool kUp>
-__device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]) {
+__device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::LDS]) {
   TileInfo ti;
   const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
   if (!find_tile(sched, p.offsets, p.E, p.ntok, C::BM, ti)) return;
@@ -395,8 +418,8 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter);
   const int N = kUp ? (shared ? p.inter_s : p.inter) : p.dim;   // h columns / output columns
-  const int m0 = ti.mt * C::BM;
-  const int rows_left = ti.M - m0;
+  const int m0 = ti.m0;
+  const int rows_left = ti.mrows;
 
   StreamSrc<C> S;
   const int lc = tid % C::TPR, lr = tid / C::TPR;
@@ -463,7 +486,7 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
 #pragma unroll
   for (int a = 0; a < C::MT; ++a) {
     const int m = m0 + 32 * a + ml;
-    if (a >= m_active || m >= ti.M) continue;
+    if (a >= m_active || m >= m0 + rows_left) continue;
     if (kUp) {
       uint16_t* hrow = shared ? static_cast<uint16_t*>(p.hs) + (size_t)m * N
                               : static_cast<uint16_t*>(p.h) + (size_t)(ti.row0 + m) * N;
@@ -504,7 +527,7 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[2][C::LDS]
 // epilogue quantises h per 1x128 block: the 8 waves' 16-column slices of a
 // token row form exactly one block, so the amax is reduced across waves in LDS.
 // ---------------------------------------------------------------------------
-using F8 = SCfg<192, 8, 2, 2>;   // 192 tokens, 8 waves x 32 weight rows, ring of 2
+using F8 = SCfg<192, 8, 2, 1>;   // 192 tokens, 8 waves x 32 weight rows, ring of 2
 constexpr int kF8MT = F8::BM / 32;
 
 struct StreamSrcF8 {
@@ -517,17 +540,18 @@ struct StreamSrcF8 {
 };
 
 template <int MT>
-__device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (&sxs)[2][F8::BM],
+__device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], float2 (&sxs)[F8::NB][F8::BM],
                                                   const StreamSrcF8& S, int nk,
                                                   f32x16_t (&acc)[kF8MT]) {
   constexpr int XL = std::min(F8::XLOADS, (32 * MT + F8::ROWS_PER_PASS - 1) / F8::ROWS_PER_PASS);
   constexpr int RING = F8::RING;
-  constexpr int UNROLL = std::lcm(RING, 2);
+  constexpr int XD = F8::XD, NB = F8::NB, D = F8::D;
+  constexpr int UNROLL = F8::UNROLL;
   const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
   i32x8_t_ wr[RING][2];          // [slice % RING][K half]
   float wsc[RING][2];            // [slice % RING][D half]
-  uint4 xr[2][F8::XLOADS];
-  float xsr[2][F8::XLOADS];
+  uint4 xr[XD][F8::XLOADS];      // token slices between load and LDS store: [slice % XD]
+  float xsr[XD][F8::XLOADS];
   float sprev[MT][2];            // units of the accumulator halves
 #pragma unroll
   for (int a = 0; a < MT; ++a) sprev[a][0] = sprev[a][1] = 1.f;
@@ -554,47 +578,64 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (
     for (int i = 0; i < XL; ++i) {
       static_assert(F8::BM % F8::ROWS_PER_PASS == 0, "every token load pass lands inside the tile");
       *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + F8::ROWS_PER_PASS * i * F8::STRIDE]) = src[i];
-      sxs[buf][(threadIdx.x >> 3) + F8::ROWS_PER_PASS * i] = sc[i];   // equal values from the row's 8 lanes
+      // (scale, 1/scale), equal values from the row's 8 lanes
+      sxs[buf][(threadIdx.x >> 3) + F8::ROWS_PER_PASS * i] = make_float2(sc[i], __builtin_amdgcn_rcpf(sc[i]));
     }
   };
-  xload(xr[0], xsr[0], 0);
-  xload(xr[1], xsr[1], 1);
+  // the token staging of the bf16 stream loop: slice j in LDS buffer j % NB,
+  // slice kt+D stored after step kt, one barrier every D steps
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    xload(xr[j % XD], xsr[j % XD], j);
+    xstore(xr[j % XD], xsr[j % XD], j);
+  }
+#pragma unroll
+  for (int j = D; j < D + XD - 1; ++j) xload(xr[j % XD], xsr[j % XD], j);
 #pragma unroll
   for (int j = 0; j < RING - 1; ++j) wload(wr[j], wsc[j], j);
-  xstore(xr[0], xsr[0], 0);
   __syncthreads();
   auto step = [&](int kt, auto R) {
     constexpr int r = decltype(R)::value;
     constexpr int ws = r % RING;
-    xload(xr[r & 1], xsr[r & 1], kt + 2);
+    constexpr int xl = (r + D - 1 + XD) % XD;
+    xload(xr[xl], xsr[xl], kt + D - 1 + XD);
     wload(wr[(ws + RING - 1) % RING], wsc[(ws + RING - 1) % RING], kt + RING - 1);
     __builtin_amdgcn_sched_barrier(0);
-    const char* sb = sx[r & 1] + fr * F8::STRIDE + 32 * fg;
-    const float* sbs = sxs[r & 1] + fr;
+    const char* sb = sx[kt % NB] + fr * F8::STRIDE + 32 * fg;
+    const float2* sbs = sxs[kt % NB] + fr;
+    const float iw[2] = {__builtin_amdgcn_rcpf(wsc[ws][0]), __builtin_amdgcn_rcpf(wsc[ws][1])};
+    // the fragments and scales of sub-tile a+1 are read from LDS while
+    // sub-tile a is rescaled and multiplied
+    i32x8_t_ bx[2][2];
+    float2 xsc[2];
+    auto frag = [&](int a, int b) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bx[b][j] = *reinterpret_cast<const i32x8_t_*>(sb + 32 * a * F8::STRIDE + 64 * j);
+      xsc[b] = sbs[32 * a];
+    };
+    frag(0, 0);
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
-      i32x8_t_ bx[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bx[j] = *reinterpret_cast<const i32x8_t_*>(sb + 32 * a * F8::STRIDE + 64 * j);
-      const float xsc = sbs[32 * a];
+      if (a + 1 < MT) frag(a + 1, (a + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const float2 xs = xsc[a & 1];
       float ratio[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float sc = wsc[ws][h] * xsc;
-        ratio[h] = __builtin_amdgcn_rcpf(sc) * sprev[a][h];
-        sprev[a][h] = sc;
+      for (int h = 0; h < 2; ++h) {   // s_prev / s with s = w_scale * a_scale
+        ratio[h] = sprev[a][h] * iw[h] * xs.y;
+        sprev[a][h] = wsc[ws][h] * xs.x;
       }
       f32x16_t c = acc[a];
 #pragma unroll
       for (int i = 0; i < 16; ++i) c[i] *= ratio[i >> 3];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][j], bx[j], c, 0, 0, 0, 127, 0, 127);
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][j], bx[a & 1][j], c, 0, 0, 0, 127, 0, 127);
       acc[a] = c;
-      __builtin_amdgcn_sched_barrier(0);   // one token sub-tile's operands live at a time
+      __builtin_amdgcn_sched_barrier(0);
     }
-    xstore(xr[(r + 1) & 1], xsr[(r + 1) & 1], (r + 1) & 1);
-    __syncthreads();
+    xstore(xr[(r + D) % XD], xsr[(r + D) % XD], (kt + D) % NB);
+    if (r % D == D - 1) __syncthreads();
   };
   auto body = [&](int kt0, auto... R) { (step(kt0 + decltype(R)::value, R), ...); };
   auto tail = [&](int kt0, auto... R) {
@@ -615,8 +656,8 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[2][F8::LDS], float (
 template <bool kUp>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_fp8_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[2][F8::LDS];
-  __shared__ float sxs[2][F8::BM];
+  __shared__ __attribute__((aligned(16))) char sx[F8::NB][F8::LDS];
+  __shared__ float2 sxs[F8::NB][F8::BM];
   __shared__ float wamax[F8::WAVES][F8::BM];
   TileInfo ti;
   const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
@@ -625,8 +666,8 @@ void stream_fp8_kernel(FfnProblem p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter), KB = K / 128;
   const int N = kUp ? (shared ? p.inter_s : p.inter) : p.dim;
-  const int m0 = ti.mt * F8::BM;
-  const int rows_left = ti.M - m0;
+  const int m0 = ti.m0;
+  const int rows_left = ti.mrows;
 
   StreamSrcF8 S;
   const int lc = tid & 7, lr = tid >> 3;
@@ -701,7 +742,7 @@ void stream_fp8_kernel(FfnProblem p) {
 #pragma unroll
     for (int a = 0; a < kF8MT; ++a) {
       const int m = m0 + 32 * a + ml;
-      if (a >= m_active || m >= ti.M) continue;
+      if (a >= m_active || m >= m0 + rows_left) continue;
       float am = 0.f;
 #pragma unroll
       for (int w = 0; w < F8::WAVES; ++w) am = fmaxf(am, wamax[w][32 * a + ml]);
@@ -725,7 +766,7 @@ void stream_fp8_kernel(FfnProblem p) {
 #pragma unroll
     for (int a = 0; a < kF8MT; ++a) {
       const int m = m0 + 32 * a + ml;
-      if (a >= m_active || m >= ti.M) continue;
+      if (a >= m_active || m >= m0 + rows_left) continue;
       uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) +
                        (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
 #pragma unroll
@@ -740,21 +781,21 @@ void stream_fp8_kernel(FfnProblem p) {
 template <bool kUp>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[2][SBig::LDS];
+  __shared__ __attribute__((aligned(16))) char sx[SBig::NB][SBig::LDS];
   stream_tile<SBig, kUp>(p, sx);
 }
 
 template <bool kUp>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_huge_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[2][SHuge::LDS];
+  __shared__ __attribute__((aligned(16))) char sx[SHuge::NB][SHuge::LDS];
   stream_tile<SHuge, kUp>(p, sx);
 }
 
 template <bool kUp>
 __global__ __launch_bounds__(256, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void stream_mid_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[2][SMid::LDS];
+  __shared__ __attribute__((aligned(16))) char sx[SMid::NB][SMid::LDS];
   stream_tile<SMid, kUp>(p, sx);
 }
 
@@ -825,7 +866,7 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int nbase = ti.nt * 128 + wave * 32;          // N % 128 == 0: always inside
-  const int mi = min(ti.mt * 16 + r, ti.M - 1);
+  const int mi = ti.m0 + min(r, ti.mrows - 1);
   const int tok = shared ? mi : p.sorted_token[ti.row0 + mi];
   const char* bp = reinterpret_cast<const char*>(p.xq + (size_t)tok * K) + 32 * grp;
   const float* bsc = p.xs + (size_t)tok * KB;
@@ -885,8 +926,8 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   __syncthreads();
   amax = fmaxf(fmaxf(wamax[0][r], wamax[1][r]), fmaxf(wamax[2][r], wamax[3][r]));
   const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-  const int m = ti.mt * 16 + r;
-  if (m < ti.M) {
+  const int m = ti.m0 + r;
+  if (r < ti.mrows) {
     const size_t row = shared ? (size_t)m : (size_t)(ti.row0 + m);
     uint8_t* hq = static_cast<uint8_t*>(shared ? p.hs : p.h) + row * N;
     float* hsc = (shared ? p.hsscale : p.hscale) + row * (N / 128);
@@ -913,7 +954,7 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   const int r = lane & 15, grp = lane >> 4;
   const int nbase = ti.nt * kDnBN + wave * 16 * kDnNT;
   if (nbase >= N) return;
-  const int mi = min(ti.mt * 16 + r, ti.M - 1);
+  const int mi = ti.m0 + min(r, ti.mrows - 1);
   const size_t hrow = shared ? (size_t)mi : (size_t)(ti.row0 + mi);
   const char* bp = reinterpret_cast<const char*>(static_cast<const uint8_t*>(shared ? p.hs : p.h) + hrow * K) + 32 * grp;
   const float* bsc = (shared ? p.hsscale : p.hscale) + hrow * KB;
@@ -957,8 +998,8 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
     if (kb + 2 < KB) load(0, kb + 2);
     if (kb + 1 < KB) comp(1, kb + 1);
   }
-  const int m = ti.mt * 16 + r;
-  if (m < ti.M) {
+  const int m = ti.m0 + r;
+  if (r < ti.mrows) {
     uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) + (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
 #pragma unroll
     for (int j = 0; j < kDnNT; ++j) {

@@ -62,6 +62,9 @@ hipError_t launch_quant_x(const uint16_t* x, int ntok, int dim, uint8_t* xq, flo
 hipError_t launch_pack_weights(const uint8_t* src, int64_t rows, int64_t row_bytes, uint8_t* dst,
                                hipStream_t st);
 
+// calib.hip (measurement only): one streaming read of bytes (multiple of 16)
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+
 // combine.hip
 // layer_acc: accumulate in the layer dtype over the experts in ascending id
 // (rows ascend with the expert id), casting after every addition.

@@ -372,6 +372,14 @@ moe_status moe_pack_weights(const void* src, int64_t rows, int64_t row_bytes, vo
   return e == hipSuccess ? MOE_OK : hip_fail(e, "pack launch");
 }
 
+moe_status moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  g_err.clear();
+  if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+  if (bytes == 0 || bytes % 16 != 0) return fail(MOE_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  hipError_t e = moe::launch_stream_read(buf, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "stream-read launch");
+}
+
 moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_weights* w,
                        void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
                        void* workspace, size_t workspace_bytes, void* stream) {

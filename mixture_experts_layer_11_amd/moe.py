@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "moe_abi_version": (ctypes.c_int32, []),
         "moe_quant_fp8": (st, [_VP, i64, ctypes.c_int32, _VP, _VP, _VP]),
         "moe_pack_weights": (st, [_VP, i64, i64, _VP, _VP]),
+        "moe_stream_read": (st, [_VP, sz, _VP, _VP]),
         "moe_profile_start": (st, [ctypes.c_int32]),
         "moe_profile_stop": (st, [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float),
                                   ctypes.POINTER(ctypes.c_float)]),
@@ -92,7 +93,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_status_string", "moe_last_error", "moe_abi_version",
-           "moe_profile_start", "moe_profile_stop", "moe_quant_fp8", "moe_pack_weights")
+           "moe_profile_start", "moe_profile_stop", "moe_quant_fp8", "moe_pack_weights",
+           "moe_stream_read")
 
 
 def status_string(s: int) -> str:
@@ -259,6 +261,12 @@ def moe_pack_weights(w, stream=None):
     out = torch.empty_like(w)
     _check(lib().moe_pack_weights(_ptr(w), rows, row_bytes, _ptr(out), _stream(stream)))
     return out
+
+
+def moe_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Enqueue one streaming read of every byte of buf (measurement helper)."""
+    _check(lib().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(stream)))
 
 
 def moe_profile_start(max_calls: int):

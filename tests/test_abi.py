@@ -155,6 +155,16 @@ def test_pack_weights_rejects_null_and_aliasing():
     assert L.moe_pack_weights(None, 0, 64, None, None) == moe.MOE_OK     # nothing to do
 
 
+def test_stream_read_rejects_bad_arguments():
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    assert L.moe_stream_read(None, 64, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_stream_read(fake, 64, None, None) == moe.MOE_ERR_INVALID_ARG
+    for n in (0, 8, 100):
+        assert L.moe_stream_read(fake, n, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert "multiple of 16" in moe.lib().moe_last_error().decode()
+
+
 def test_zero_tokens_is_a_noop():
     L = moe.lib()
     for cfg in SMALL_CONFIGS:
