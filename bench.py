@@ -65,11 +65,11 @@ def up_kernel_name(cfg):
         return "moe::stream_fp8_kernel<true>" if R >= 48 * E else "moe::up_skinny_fp8_kernel"
     if cfg.w_dtype == "bf16" and cfg.dim % 64 == 0 and cfg.inter % 64 == 0 and cfg.inter_shared % 64 == 0:
         if R >= 384 * E:
-            return "moe::stream_huge_bf16_kernel<true>"
+            return "moe::stream_bf16_kernel<256-token tiles, up>"
         if R >= 128 * E:
-            return "moe::stream_bf16_kernel<true>"
+            return "moe::stream_bf16_kernel<192-token tiles, up>"
         if R >= 48 * E:
-            return "moe::stream_mid_bf16_kernel<true>"
+            return "moe::stream_bf16_kernel<64-token tiles, up>"
     return "moe::up_skinny_kernel<%s>" % ("float" if cfg.w_dtype == "f32" else "unsigned short")
 
 

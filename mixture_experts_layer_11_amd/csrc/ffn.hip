@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 // ---------------------------------------------------------------------------
 // Tile shape of the stream kernel: BM token rows, WAVES waves of 32 weight
 // rows each, 64-element K slices.
-template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4>
+template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4, int WPE_ = 2>
 struct SCfg {
   static constexpr int BM = BM_;
   static constexpr int WAVES = WAVES_;
@@ -309,11 +309,12 @@ struct SCfg {
   static constexpr int NB = NB_;                   // token LDS buffers
   static constexpr int D = NB / 2;                 // steps per barrier; slice kt+D is stored after step kt
   static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), D);   // steps with compile-time stage indices
+  static constexpr int WPE = WPE_;                 // waves per SIMD (workgroups per CU * WAVES / 4)
   static_assert(NB == 2 || NB == 4, "two or four token buffers");
 };
 using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
 using SHuge = SCfg<256, 8, 2, 2>; // experts of many hundred tokens: larger tiles, shallower rings
-using SMid = SCfg<64, 4, 4>;   // 64-token tiles, three workgroups per CU
+using SMid = SCfg<64, 4, 4, 2, 4, 3>;   // 64-token tiles, three workgroups per CU
 
 template <class C>
 struct StreamSrc {
@@ -778,25 +779,11 @@ void stream_fp8_kernel(FfnProblem p) {
   }
 }
 
-template <bool kUp>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <class C, bool kUp>
+__global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void stream_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[SBig::NB][SBig::LDS];
-  stream_tile<SBig, kUp>(p, sx);
-}
-
-template <bool kUp>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void stream_huge_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[SHuge::NB][SHuge::LDS];
-  stream_tile<SHuge, kUp>(p, sx);
-}
-
-template <bool kUp>
-__global__ __launch_bounds__(256, 3) __attribute__((amdgpu_waves_per_eu(3, 3)))
-void stream_mid_bf16_kernel(FfnProblem p) {
-  __shared__ __attribute__((aligned(16))) char sx[SMid::NB][SMid::LDS];
-  stream_tile<SMid, kUp>(p, sx);
+  __shared__ __attribute__((aligned(16))) char sx[C::NB][C::LDS];
+  stream_tile<C, kUp>(p, sx);
 }
 
 // ---------------------------------------------------------------------------
@@ -1071,9 +1058,9 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   }
   mark(0);
   if (t == Tiles::Big && f8) stream_fp8_kernel<true><<<g_up, F8::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Huge) stream_huge_bf16_kernel<true><<<g_up, SHuge::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big) stream_bf16_kernel<true><<<g_up, SBig::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Mid) stream_mid_bf16_kernel<true><<<g_up, SMid::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, true><<<g_up, SHuge::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<SBig, true><<<g_up, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Mid) stream_bf16_kernel<SMid, true><<<g_up, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
   else if (p.wkind == WKind::BF16) up_skinny_kernel<uint16_t><<<g_up, 256, 0, st>>>(q);
   else up_skinny_kernel<float><<<g_up, 256, 0, st>>>(q);
@@ -1081,9 +1068,9 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
   mark(2);
   if (t == Tiles::Big && f8) stream_fp8_kernel<false><<<g_dn, F8::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Huge) stream_huge_bf16_kernel<false><<<g_dn, SHuge::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big) stream_bf16_kernel<false><<<g_dn, SBig::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Mid) stream_mid_bf16_kernel<false><<<g_dn, SMid::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false><<<g_dn, SHuge::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<SBig, false><<<g_dn, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Mid) stream_bf16_kernel<SMid, false><<<g_dn, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);
   else if (p.wkind == WKind::BF16) down_skinny_kernel<uint16_t><<<g_dn, 256, 0, st>>>(q);
   else down_skinny_kernel<float><<<g_dn, 256, 0, st>>>(q);

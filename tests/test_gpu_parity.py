@@ -376,3 +376,16 @@ def test_forward_graph_replays_match_eager(ci, layers):
         g.replay()
         _sync()
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# measurement helper: one streaming read, nothing written for zero data
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 64 << 20])
+def test_stream_read_leaves_sink_for_zero_data(nbytes):
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    moe.moe_stream_read(buf, sink)
+    _sync()
+    assert int(sink.item()) == 7
