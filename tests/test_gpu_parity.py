@@ -148,6 +148,49 @@ def test_expert_ffn_parity(cfg, layers):
         assert mx <= bar(cfg)[0] and mean <= bar(cfg)[1], (mx, mean)
 
 
+# Hand-made dispatches whose expert sizes straddle the m-tile boundaries of
+# each tile kind (the batch size R = T*topk picks the kind: 16-token, 64-token,
+# 192-token and 256-token bf16 tiles, 192-token fp8 tiles).  An expert of M
+# rows runs as ceil(M / BM) m-tiles of equal size, the last taking the rest.
+TILE_CASES = [
+    ("mid_bf16", dict(E=8, topk=2, w_dtype="bf16"), [65, 64, 63, 129, 0, 1, 150, 128]),
+    ("big_bf16", dict(E=4, topk=2, w_dtype="bf16"), [193, 0, 385, 622]),
+    ("huge_bf16", dict(E=4, topk=2, w_dtype="bf16"), [257, 513, 1, 829]),
+    ("skinny_bf16", dict(E=8, topk=2, w_dtype="bf16"), [17, 0, 16, 15, 33, 1, 2, 0]),
+    ("big_fp8", dict(E=4, topk=2, w_dtype="fp8"), [193, 385, 1, 21]),
+]
+
+
+@pytest.mark.parametrize("name,kw,counts", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+def test_expert_ffn_tile_boundaries(name, kw, counts):
+    R = sum(counts)
+    T = R // kw["topk"]
+    cfg = tiny_cfg(name, T=T, dim=256, inter=256, inter_shared=128, n_groups=1,
+                   act_dtype="bf16", router_dtype="bf16", seed=4242, **kw)
+    layer = inputs.draw_layer(cfg)
+    dw = moe.upload_layer(layer)
+    rng = np.random.default_rng(99)
+    sorted_token = np.concatenate([np.sort(rng.choice(T, size=c, replace=c > T)) for c in counts]
+                                  ).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    p = moe.Params.from_config(cfg)
+    ws = moe.alloc_workspace(p, T)
+    out, _ = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
+                                torch.from_numpy(offsets).to(DEV), dw, ws)
+    _sync()
+    out = moe.to_host_values(out)
+    xv = oracle.moe_oracle.decode_act(layer.x, cfg.act_dtype)
+    for e, c in enumerate(counts):
+        a, b = offsets[e], offsets[e + 1]
+        if a == b:
+            continue
+        w1, w3, w2, s1, s3, s2 = expert_fn(layer)(e)
+        ref = oracle.expert_ffn(xv[sorted_token[a:b]], w1, w3, w2, cfg.w_dtype, cfg.act_dtype,
+                                s1, s3, s2)
+        mx, mean = rel_errors(out[a:b], ref)
+        assert mx <= bar(cfg)[0] and mean <= bar(cfg)[1], (e, c, mx, mean)
+
+
 # ---------------------------------------------------------------------------
 # fp8 activation quantiser (bit-exact codes and scales)
 # ---------------------------------------------------------------------------
