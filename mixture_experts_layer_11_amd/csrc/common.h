@@ -45,7 +45,10 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
   return static_cast<uint8_t>(code == 0 ? 0 : (code | sign));
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// silu(a) = a * sigmoid(a), with the hardware reciprocal (about 1 ulp) in place
+// of an IEEE division: the result is rounded to bf16 or e4m3 next.  exp(-a)
+// overflowing to inf gives a * 0, the limit.
+__device__ __forceinline__ float silu(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // ---- wave reductions ------------------------------------------------------
 

@@ -735,7 +735,10 @@ void stream_fp8_kernel(FfnProblem p) {
     for (int a = 0; a < kF8MT; ++a) {
       float am = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(silu(acc[a][i]) * acc[a][8 + i]));
+      for (int i = 0; i < 8; ++i) {   // h replaces the W1 half of the accumulator
+        acc[a][i] = silu(acc[a][i]) * acc[a][8 + i];
+        am = fmaxf(am, fabsf(acc[a][i]));
+      }
       am = fmaxf(am, __shfl_xor(am, 32, kWave));
       if (fg == 0) wamax[wave][32 * a + ml] = am;
     }
@@ -754,10 +757,8 @@ void stream_fp8_kernel(FfnProblem p) {
       for (int q = 0; q < 2; ++q) {   // rows 8q + rg + [0,4) of W1, 16 + the same of W3
         uint32_t pk = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = silu(acc[a][4 * q + i]) * acc[a][8 + 4 * q + i];
-          pk |= (uint32_t)f32_to_e4m3(__fdiv_rn(v, scale)) << (8 * i);
-        }
+        for (int i = 0; i < 4; ++i)
+          pk |= (uint32_t)f32_to_e4m3(__fdiv_rn(acc[a][4 * q + i], scale)) << (8 * i);
         *reinterpret_cast<uint32_t*>(hq + ncol0 + 8 * q + rg) = pk;
       }
       if (wave == 0 && fg == 0) (shared ? p.hsscale : p.hscale)[row * (N / 128) + ti.nt] = scale;
