@@ -101,16 +101,25 @@ def workload_numbers(cfg, counts, experts=None):
                 up_flops=up_flops, per_expert_up_bytes=2 * (I * dim * wsz + scale_b))
 
 
+KERNEL_SOURCES = ("ffn.hip", "common.h", "kernels.h")   # what the expert kernels are built from
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "mixture_experts_layer_11_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def traffic_for(kernel, workload):
     """HBM traffic from the committed rocprofv3 counter runs, if the kernel
-    source is unchanged since they were taken (else None)."""
+    sources are unchanged since they were taken (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "mixture_experts_layer_11_amd", "csrc", "ffn.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = kernel_source_sha()
     ent = rec.get(f"{kernel}@{workload}")
     if not ent or ent.get("source_sha") != sha:
         return None
