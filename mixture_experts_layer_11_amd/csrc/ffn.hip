@@ -135,7 +135,7 @@ __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* b
   for (int u = 0; u < U; ++u) {
     b0[u] = ldg16(bp + 64 * u);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) a0[u][j] = ldg16(ap[j] + kChunkStride * u);
+    for (int j = 0; j < NA; ++j) a0[u][j] = ldg16_stream(ap[j] + kChunkStride * u);
   }
   for (int c = 0; c < nchunk; c += 2 * U) {
     if (c + U < nchunk) {
@@ -143,7 +143,7 @@ __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* b
       for (int u = 0; u < U; ++u) {
         b1[u] = ldg16(bp + 64 * (c + U + u));
 #pragma unroll
-        for (int j = 0; j < NA; ++j) a1[u][j] = ldg16(ap[j] + kChunkStride * (c + U + u));
+        for (int j = 0; j < NA; ++j) a1[u][j] = ldg16_stream(ap[j] + kChunkStride * (c + U + u));
       }
     }
 #pragma unroll
@@ -155,7 +155,7 @@ __device__ __forceinline__ void kloop(const char* const (&ap)[NA], const char* b
       for (int u = 0; u < U; ++u) {
         b0[u] = ldg16(bp + 64 * (c + 2 * U + u));
 #pragma unroll
-        for (int j = 0; j < NA; ++j) a0[u][j] = ldg16(ap[j] + kChunkStride * (c + 2 * U + u));
+        for (int j = 0; j < NA; ++j) a0[u][j] = ldg16_stream(ap[j] + kChunkStride * (c + 2 * U + u));
       }
     }
     if (c + U < nchunk) {
@@ -276,11 +276,12 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 //     flight); for the up projection rows 0-15 are W1 rows and rows 16-31 the
 //     same rows of W3, so a lane's result elements i and i+8 are the two
 //     branches of one h column and SwiGLU needs no data exchange.
-//   B operand = token rows, staged in LDS (double-buffered) and read by all 8
-//     waves: the slice of every n-tile of an expert is the same, so it is
-//     L2-resident.
+//   B operand = token rows, staged in LDS (four buffers, one workgroup
+//     barrier per two slices) and read by all 8 waves: the slice of every
+//     n-tile of an expert is the same, so it is mostly L2-resident.
 // Loaded HBM latency is several microseconds, so weights run three 64-element
-// slices ahead and token slices two (in registers until their LDS store).
+// slices ahead and token slices are loaded into registers a few steps before
+// their LDS store.
 // Memory counters retire in issue order; each step issues its token slice
 // before its weight slice, so waiting for a token slice to store never forces
 // a newer weight slice to land early.  The K loop is instantiated for the
@@ -875,8 +876,8 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   auto load = [&](int s, int kb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[s][j][0] = ldg16(ap[j] + 2 * kChunkStride * kb);
-      a[s][j][1] = ldg16(ap[j] + 2 * kChunkStride * kb + 256);
+      a[s][j][0] = ldg16_stream(ap[j] + 2 * kChunkStride * kb);
+      a[s][j][1] = ldg16_stream(ap[j] + 2 * kChunkStride * kb + 256);
     }
     b[s][0] = ldg16(bp + 128 * kb);
     b[s][1] = ldg16(bp + 128 * kb + 16);
@@ -963,8 +964,8 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   auto load = [&](int s, int kb) {
 #pragma unroll
     for (int j = 0; j < kDnNT; ++j) {
-      a[s][j][0] = ldg16(ap[j] + 2 * kChunkStride * kb);
-      a[s][j][1] = ldg16(ap[j] + 2 * kChunkStride * kb + 256);
+      a[s][j][0] = ldg16_stream(ap[j] + 2 * kChunkStride * kb);
+      a[s][j][1] = ldg16_stream(ap[j] + 2 * kChunkStride * kb + 256);
     }
     b[s][0] = ldg16(bp + 128 * kb);
     b[s][1] = ldg16(bp + 128 * kb + 16);
