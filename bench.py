@@ -11,6 +11,11 @@ W1 and W3 of every expert that receives a token, two thirds of the layer's
 weight bytes).  Its algorithmic bytes per launch divided by its average
 launch time (HIP events recorded around that launch on its own stream during
 the timed steps) against the MI355X HBM peak of 8 TB/s.
+
+measured_peaks: what the machine delivers, next to the published peaks - the
+library's streaming-read kernel over 4 GiB and a dense 8192^3 bf16 GEMM.
+--graph times replays of one forward captured in a HIP graph instead of eager
+calls.
 """
 
 from __future__ import annotations
