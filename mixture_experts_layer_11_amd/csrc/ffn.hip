@@ -314,7 +314,7 @@ struct SCfg {
   static_assert(NB == 2 || NB == 4, "two or four token buffers");
 };
 using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
-using SHuge = SCfg<256, 8, 2, 2>; // experts of many hundred tokens: larger tiles, shallower rings
+using SHuge = SCfg<256, 8, 2, 1>; // experts of many hundred tokens: larger tiles, shallower rings
 using SMid = SCfg<64, 4, 4, 2, 4, 3>;   // 64-token tiles, three workgroups per CU
 
 template <class C>
