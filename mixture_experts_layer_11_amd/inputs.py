@@ -98,7 +98,7 @@ CONFIGS = [
 
 # Small shapes for parity tests: several MFMA tiles, ragged token counts.
 SMALL_CONFIGS = [
-    CONFIGS[0],
+    next(c for c in CONFIGS if c.name == "c0_tiny_fp32"),
     MoEConfig("s1_mini_dsv3_bf16", T=333, dim=512, E=32, n_groups=4, topk_groups=2, topk=4,
               score_func="sigmoid", route_scale=2.5, bias_range=0.05, inter=256,
               inter_shared=256, act_dtype="bf16", w_dtype="bf16", router_dtype="bf16",

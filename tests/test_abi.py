@@ -9,7 +9,7 @@ import re
 import pytest
 
 from mixture_experts_layer_11_amd import moe
-from mixture_experts_layer_11_amd.inputs import CONFIGS, SMALL_CONFIGS
+from mixture_experts_layer_11_amd.inputs import SMALL_CONFIGS, config_by_name
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
@@ -43,7 +43,7 @@ def test_status_strings():
 
 
 def _p(**kw):
-    base = moe.Params.from_config(CONFIGS[1])
+    base = moe.Params.from_config(config_by_name("c1"))
     for k, v in kw.items():
         setattr(base, k, v)
     return base

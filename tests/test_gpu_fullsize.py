@@ -14,25 +14,28 @@ from tests.test_gpu_parity import forward_and_check
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {0: None, 1: 24, 2: 12, 3: 384, 4: 12}
+# sampled tokens per workload (None: every token)
+SAMPLE = {"c0": None, "c1": 24, "c2": 12, "c3": 384, "c4": 12}
 
 
 def progress(msg):
-    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    if os.path.isdir(d):
-        with open(os.path.join(d, "progress.log"), "a") as f:
+    """Progress lines for long runs, appended to $MOE_PROGRESS_FILE when set."""
+    path = os.environ.get("MOE_PROGRESS_FILE")
+    if path:
+        with open(path, "a") as f:
             f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
-def test_forward_full_size(ci):
-    cfg = inputs.CONFIGS[ci]
+@pytest.mark.parametrize("name", list(SAMPLE))
+def test_forward_full_size(name):
+    cfg = inputs.config_by_name(name)
+    ci = list(SAMPLE).index(name)
     progress(f"{cfg.name}: drawing inputs")
     layer = inputs.draw_layer(cfg)
     progress(f"{cfg.name}: uploading")
     dw = moe.upload_layer(layer)
-    n = SAMPLE[ci]
+    n = SAMPLE[name]
     tokens = None
     if n is not None:
         rng = np.random.default_rng(ci)

@@ -146,7 +146,7 @@ def test_activation_quantisation_1x128():
 def test_router_parameter_count_golden():
     with open(os.path.join(GOLDEN, "router_params.json")) as f:
         g = json.load(f)
-    c1 = inputs.CONFIGS[1]
+    c1 = inputs.config_by_name("c1")
     assert c1.dim == g["dim"] and c1.E == g["n_routed_experts"]
     wr, _, _ = inputs.draw_router(c1)
     assert wr.shape == (g["n_routed_experts"], g["dim"])          # [out, in]
@@ -157,5 +157,5 @@ def test_router_parameter_count_golden():
 def test_combine_shapes_golden():
     with open(os.path.join(GOLDEN, "combine_shapes.json")) as f:
         g = json.load(f)
-    for c in (inputs.CONFIGS[1], inputs.CONFIGS[2], inputs.CONFIGS[4]):
+    for c in (inputs.config_by_name("c1"), inputs.config_by_name("c2"), inputs.config_by_name("c4")):
         assert c.E == g["n_routed_experts"] and c.dim == g["dim"]

@@ -191,7 +191,7 @@ def test_bias_affects_selection_not_weights():
 
 
 def test_c0_gate_invariants():
-    layer = inputs.draw_layer(inputs.CONFIGS[0])
+    layer = inputs.draw_layer(inputs.config_by_name("c0"))
     w, idx, info = gate_oracle(layer)
     c = layer.cfg
     check_select_invariants(info["s"], layer.bias, c.n_groups, c.topk_groups, c.topk, idx)
@@ -278,7 +278,7 @@ def test_dense_formula_matches_sparse_loop():
     for cfg in (tiny_cfg(T=24), tiny_cfg(T=17, n_groups=1, topk=3, score_func="softmax",
                                           bias_range=None, act_dtype="bf16", w_dtype="bf16",
                                           router_dtype="bf16", inter_shared=0),
-                inputs.CONFIGS[0]):
+                inputs.config_by_name("c0")):
         layer = inputs.draw_layer(cfg)
         r = run_oracle(layer)
         d = oracle.moe_forward_dense(layer.x, layer.wr, layer.bias, expert_fn(layer),
