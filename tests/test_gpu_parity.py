@@ -161,12 +161,22 @@ TILE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,kw,counts", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+# the shortest K loops: one or two steps per tile (64-wide bf16, 128-wide fp8)
+SHORT_K_CASES = [
+    ("big_bf16_k64", dict(E=4, topk=2, w_dtype="bf16", dim=64, inter=64, inter_shared=64), [193, 0, 385, 622]),
+    ("huge_bf16_k128", dict(E=4, topk=2, w_dtype="bf16", dim=128, inter=64, inter_shared=128), [257, 513, 1, 829]),
+    ("mid_bf16_k64", dict(E=8, topk=2, w_dtype="bf16", dim=64, inter=128, inter_shared=64), [65, 64, 63, 129, 0, 1, 150, 128]),
+    ("big_fp8_k128", dict(E=4, topk=2, w_dtype="fp8", dim=128, inter=128, inter_shared=128), [193, 385, 1, 21]),
+]
+
+
+@pytest.mark.parametrize("name,kw,counts", TILE_CASES + SHORT_K_CASES,
+                         ids=[c[0] for c in TILE_CASES + SHORT_K_CASES])
 def test_expert_ffn_tile_boundaries(name, kw, counts):
     R = sum(counts)
     T = R // kw["topk"]
-    cfg = tiny_cfg(name, T=T, dim=256, inter=256, inter_shared=128, n_groups=1,
-                   act_dtype="bf16", router_dtype="bf16", seed=4242, **kw)
+    kw = dict(dict(dim=256, inter=256, inter_shared=128), **kw)
+    cfg = tiny_cfg(name, T=T, n_groups=1, act_dtype="bf16", router_dtype="bf16", seed=4242, **kw)
     layer = inputs.draw_layer(cfg)
     dw = moe.upload_layer(layer)
     rng = np.random.default_rng(99)
