@@ -1016,18 +1016,22 @@ size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool ac
 
 enum class Tiles { Skinny, Mid, Big, Huge };
 
-// Tile shape for a batch: 16-token skinny tiles while experts average few
-// rows (weight streaming, no reuse to gain), 64-token tiles with several
-// workgroups per CU in between, whole-expert 192-token tiles once experts
-// average >= 128 rows.  bf16 only; widths must be multiples of 64.
+// Tile shape for a batch, on the average rows per expert R / E (thresholds
+// from batch-size sweeps on the DeepSeek-V3 shape): 16-token skinny tiles
+// below 8 rows (decode: weight streaming, each expert's weights read once);
+// from there every 16-token m-tile would re-read its expert's weights, so
+// stream tiles take over - 64-token tiles with three workgroups per CU below
+// 32 rows, whole-expert 192-token tiles up to 384 rows, 256-token tiles above
+// (hot experts of many hundred rows).  fp8 weights switch to their 192-token
+// stream tiles from 12 rows.  Stream tiles need widths that are multiples of 64.
 static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
   const long R = (long)p.ntok * p.topk;
-  if (p.wkind == WKind::FP8) return R >= 48L * p.E ? Tiles::Big : Tiles::Skinny;
+  if (p.wkind == WKind::FP8) return R >= 12L * p.E ? Tiles::Big : Tiles::Skinny;
   if (p.wkind != WKind::BF16) return Tiles::Skinny;
   if (p.dim % 64 || p.inter % 64 || (has_shared && p.inter_s % 64)) return Tiles::Skinny;
   if (R >= 384L * p.E) return Tiles::Huge;
-  if (R >= 128L * p.E) return Tiles::Big;
-  if (R >= 48L * p.E) return Tiles::Mid;
+  if (R >= 32L * p.E) return Tiles::Big;
+  if (R >= 8L * p.E) return Tiles::Mid;
   return Tiles::Skinny;
 }
 

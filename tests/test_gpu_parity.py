@@ -149,15 +149,18 @@ def test_expert_ffn_parity(cfg, layers):
 
 
 # Hand-made dispatches whose expert sizes straddle the m-tile boundaries of
-# each tile kind (the batch size R = T*topk picks the kind: 16-token, 64-token,
-# 192-token and 256-token bf16 tiles, 192-token fp8 tiles).  An expert of M
-# rows runs as ceil(M / BM) m-tiles of equal size, the last taking the rest.
+# each tile kind (the average rows per expert R / E picks the kind: 16-token
+# tiles below 8, 64-token tiles below 32, 192-token tiles below 384, 256-token
+# tiles above; fp8 192-token tiles from 12, 16-token fp8 tiles below).  An
+# expert of M rows runs as ceil(M / BM) m-tiles of equal size, the last
+# taking the rest.
 TILE_CASES = [
-    ("mid_bf16", dict(E=8, topk=2, w_dtype="bf16"), [65, 64, 63, 129, 0, 1, 150, 128]),
+    ("mid_bf16", dict(E=8, topk=2, w_dtype="bf16"), [65, 64, 63, 29, 0, 1, 0, 0]),
     ("big_bf16", dict(E=4, topk=2, w_dtype="bf16"), [193, 0, 385, 622]),
     ("huge_bf16", dict(E=4, topk=2, w_dtype="bf16"), [257, 513, 1, 829]),
-    ("skinny_bf16", dict(E=8, topk=2, w_dtype="bf16"), [17, 0, 16, 15, 33, 1, 2, 0]),
+    ("skinny_bf16", dict(E=8, topk=2, w_dtype="bf16"), [17, 0, 16, 15, 1, 1, 2, 0]),
     ("big_fp8", dict(E=4, topk=2, w_dtype="fp8"), [193, 385, 1, 21]),
+    ("skinny_fp8", dict(E=8, topk=2, w_dtype="fp8"), [33, 0, 16, 17, 1, 1, 2, 0]),
 ]
 
 
@@ -165,7 +168,7 @@ TILE_CASES = [
 SHORT_K_CASES = [
     ("big_bf16_k64", dict(E=4, topk=2, w_dtype="bf16", dim=64, inter=64, inter_shared=64), [193, 0, 385, 622]),
     ("huge_bf16_k128", dict(E=4, topk=2, w_dtype="bf16", dim=128, inter=64, inter_shared=128), [257, 513, 1, 829]),
-    ("mid_bf16_k64", dict(E=8, topk=2, w_dtype="bf16", dim=64, inter=128, inter_shared=64), [65, 64, 63, 129, 0, 1, 150, 128]),
+    ("mid_bf16_k64", dict(E=8, topk=2, w_dtype="bf16", dim=64, inter=128, inter_shared=64), [65, 64, 63, 29, 0, 1, 0, 0]),
     ("big_fp8_k128", dict(E=4, topk=2, w_dtype="fp8", dim=128, inter=128, inter_shared=128), [193, 385, 1, 21]),
 ]
 
