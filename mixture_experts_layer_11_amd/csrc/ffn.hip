@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 // ---------------------------------------------------------------------------
 // Tile shape of the stream kernel: BM token rows, WAVES waves of 32 weight
 // rows each, 64-element K slices.
-template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4, int WPE_ = 2>
+template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4, int WPE_ = 2, bool NTW_ = false>
 struct SCfg {
   static constexpr int BM = BM_;
   static constexpr int WAVES = WAVES_;
@@ -311,11 +311,17 @@ struct SCfg {
   static constexpr int D = NB / 2;                 // steps per barrier; slice kt+D is stored after step kt
   static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), D);   // steps with compile-time stage indices
   static constexpr int WPE = WPE_;                 // waves per SIMD (workgroups per CU * WAVES / 4)
+  static constexpr bool NTW = NTW_;                // weights through non-temporal loads
   static_assert(NB == 2 || NB == 4, "two or four token buffers");
 };
 using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
 using SHuge = SCfg<256, 8, 2, 1>; // experts of many hundred tokens: larger tiles, shallower rings
-using SMid = SCfg<64, 4, 4, 2, 4, 3>;   // 64-token tiles, three workgroups per CU
+// 64-token tiles, three workgroups per CU; used while experts average fewer
+// than 32 rows, so their weights are always read non-temporally
+using SMid = SCfg<64, 4, 4, 2, 4, 3, true>;
+// 192-token tiles with non-temporal weight loads, for batches whose experts
+// fill one m-tile (each weight slice then read about once)
+using SBigNT = SCfg<192, 8, 4, 3, 4, 2, true>;
 
 template <class C>
 struct StreamSrc {
@@ -341,8 +347,10 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const St
   auto wload = [&](uint4 (&dst)[C::KS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s)   // k-step s: bytes 32s + 16*(lane/32) of the 128-byte slice
-      dst[s] = ldg16(S.w + kt * (2 * kChunkStride) + (s >> 1) * kChunkStride + (s & 1) * 512);
+    for (int s = 0; s < C::KS; ++s) {   // k-step s: bytes 32s + 16*(lane/32) of the 128-byte slice
+      const char* a = S.w + kt * (2 * kChunkStride) + (s >> 1) * kChunkStride + (s & 1) * 512;
+      dst[s] = C::NTW ? ldg16_stream(a) : ldg16(a);
+    }
   };
   auto xload = [&](uint4 (&dst)[C::XLOADS], int kt) {
     kt = kt < nk ? kt : nk - 1;
@@ -541,7 +549,7 @@ struct StreamSrcF8 {
   bool xact[F8::XLOADS];
 };
 
-template <int MT>
+template <int MT, bool kNT>
 __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], float2 (&sxs)[F8::NB][F8::BM],
                                                   const StreamSrcF8& S, int nk,
                                                   f32x16_t (&acc)[kF8MT]) {
@@ -561,8 +569,9 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint4 lo = ldg16(S.w + kt * (2 * kChunkStride) + j * kChunkStride);
-      const uint4 hi = ldg16(S.w + kt * (2 * kChunkStride) + j * kChunkStride + 256);
+      const char* a = S.w + kt * (2 * kChunkStride) + j * kChunkStride;
+      const uint4 lo = kNT ? ldg16_stream(a) : ldg16(a);
+      const uint4 hi = kNT ? ldg16_stream(a + 256) : ldg16(a + 256);
       dst[j] = i32x8_t_{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       sc[j] = S.ws[j][kt];
     }
@@ -655,7 +664,7 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
     for (int i = 0; i < 16; ++i) acc[a][i] *= sprev[a][i >> 3];
 }
 
-template <bool kUp>
+template <bool kUp, bool kNT>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_fp8_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[F8::NB][F8::LDS];
@@ -724,7 +733,7 @@ void stream_fp8_kernel(FfnProblem p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((m_active == I + 1 ? stream_fp8_kloop<I + 1>(sx, sxs, S, KB, acc) : void()), ...);
+    ((m_active == I + 1 ? stream_fp8_kloop<I + 1, kNT>(sx, sxs, S, KB, acc) : void()), ...);
   }(std::make_integer_sequence<int, kF8MT>{});
 
   // D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
@@ -1040,6 +1049,10 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const long R = (long)p.ntok * p.topk;
   const Tiles t = pick_tiles(p, has_shared);
   const bool f8 = p.wkind == WKind::FP8;
+  // stream tiles read their weights non-temporally while experts average
+  // fewer than 64 rows (one or two m-tiles each): measured faster there,
+  // slower once the m-tiles of an expert share weight slices in L2
+  const bool nt = R < 64L * p.E;
   int bm = 16, bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
   if (t == Tiles::Big && f8) bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN;
   else if (t == Tiles::Huge) bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN;
@@ -1063,8 +1076,10 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   mark(0);
-  if (t == Tiles::Big && f8) stream_fp8_kernel<true><<<g_up, F8::THREADS, 0, st>>>(q);
+  if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<true, true><<<g_up, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && f8) stream_fp8_kernel<true, false><<<g_up, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, true><<<g_up, SHuge::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, true><<<g_up, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big) stream_bf16_kernel<SBig, true><<<g_up, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_bf16_kernel<SMid, true><<<g_up, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
@@ -1073,8 +1088,10 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   mark(1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   mark(2);
-  if (t == Tiles::Big && f8) stream_fp8_kernel<false><<<g_dn, F8::THREADS, 0, st>>>(q);
+  if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<false, true><<<g_dn, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && f8) stream_fp8_kernel<false, false><<<g_dn, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false><<<g_dn, SHuge::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false><<<g_dn, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big) stream_bf16_kernel<SBig, false><<<g_dn, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_bf16_kernel<SMid, false><<<g_dn, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);
