@@ -316,9 +316,9 @@ struct SCfg {
 };
 using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
 using SHuge = SCfg<256, 8, 2, 1>; // experts of many hundred tokens: larger tiles, shallower rings
-// 64-token tiles, three workgroups per CU; used while experts average fewer
-// than 32 rows, so their weights are always read non-temporally
-using SMid = SCfg<64, 4, 4, 2, 4, 3, true>;
+// 64-token tiles of 256 weight rows (8 waves); used while experts average
+// fewer than 32 rows, so their weights are always read non-temporally
+using SMid = SCfg<64, 8, 4, 2, 4, 2, true>;
 // 192-token tiles with non-temporal weight loads, for batches whose experts
 // fill one m-tile (each weight slice then read about once)
 using SBigNT = SCfg<192, 8, 4, 3, 4, 2, true>;
