@@ -319,9 +319,10 @@ using SHuge = SCfg<256, 8, 2, 1>; // experts of many hundred tokens: larger tile
 // 64-token tiles of 256 weight rows (8 waves); used while experts average
 // fewer than 32 rows, so their weights are always read non-temporally
 using SMid = SCfg<64, 8, 4, 2, 4, 2, true>;
-// 192-token tiles with non-temporal weight loads, for batches whose experts
-// fill one m-tile (each weight slice then read about once)
-using SBigNT = SCfg<192, 8, 4, 3, 4, 2, true>;
+// 128-token tiles with non-temporal weight loads, for batches averaging
+// 32-64 rows per expert: an expert fills one m-tile, so each weight slice is
+// read about once
+using SBigNT = SCfg<128, 8, 4, 3, 4, 2, true>;
 
 template <class C>
 struct StreamSrc {
@@ -1056,6 +1057,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   int bm = 16, bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
   if (t == Tiles::Big && f8) bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN;
   else if (t == Tiles::Huge) bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN;
+  else if (t == Tiles::Big && nt) bm = SBigNT::BM, bn_up = SBigNT::UPBN, bn_dn = SBigNT::BN;
   else if (t == Tiles::Big) bm = SBig::BM, bn_up = SBig::UPBN, bn_dn = SBig::BN;
   else if (t == Tiles::Mid) bm = SMid::BM, bn_up = SMid::UPBN, bn_dn = SMid::BN;
   const int nt_up = ceil_div(p.inter, bn_up), nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
@@ -1079,7 +1081,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<true, true><<<g_up, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big && f8) stream_fp8_kernel<true, false><<<g_up, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, true><<<g_up, SHuge::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, true><<<g_up, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, true><<<g_up, SBigNT::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big) stream_bf16_kernel<SBig, true><<<g_up, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_bf16_kernel<SMid, true><<<g_up, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
@@ -1091,7 +1093,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<false, true><<<g_dn, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big && f8) stream_fp8_kernel<false, false><<<g_dn, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false><<<g_dn, SHuge::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false><<<g_dn, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false><<<g_dn, SBigNT::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big) stream_bf16_kernel<SBig, false><<<g_dn, SBig::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_bf16_kernel<SMid, false><<<g_dn, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);

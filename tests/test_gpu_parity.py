@@ -150,13 +150,15 @@ def test_expert_ffn_parity(cfg, layers):
 
 # Hand-made dispatches whose expert sizes straddle the m-tile boundaries of
 # each tile kind (the average rows per expert R / E picks the kind: 16-token
-# tiles below 8, 64-token tiles below 32, 192-token tiles below 384, 256-token
-# tiles above; fp8 192-token tiles from 12, 16-token fp8 tiles below).  An
+# tiles below 8, 64-token tiles below 32, 128-token tiles below 64, 192-token
+# tiles below 384, 256-token tiles above; fp8 192-token tiles from 12,
+# 16-token fp8 tiles below).  An
 # expert of M rows runs as ceil(M / BM) m-tiles of equal size, the last
 # taking the rest.
 TILE_CASES = [
     ("mid_bf16", dict(E=8, topk=2, w_dtype="bf16"), [65, 64, 63, 29, 0, 1, 0, 0]),
     ("big_bf16", dict(E=4, topk=2, w_dtype="bf16"), [193, 0, 385, 622]),
+    ("big_nt_bf16", dict(E=8, topk=2, w_dtype="bf16"), [129, 128, 1, 0, 65, 33, 27, 1]),
     ("huge_bf16", dict(E=4, topk=2, w_dtype="bf16"), [257, 513, 1, 829]),
     ("skinny_bf16", dict(E=8, topk=2, w_dtype="bf16"), [17, 0, 16, 15, 1, 1, 2, 0]),
     ("big_fp8", dict(E=4, topk=2, w_dtype="fp8"), [193, 385, 1, 21]),
