@@ -62,17 +62,20 @@ def parse():
 def up_kernel_name(cfg):
     """Name of the up-projection kernel the library launches for cfg (the
     library's rule, on R = T * topk routed rows: 256-token bf16 stream tiles
-    once experts average >= 384 rows, 192-token ones from 32 rows (fp8: from
-    12 rows), 64-token bf16 tiles from 8 rows, 16-token skinny tiles below;
-    bf16 tiles need widths that are multiples of 64)."""
+    once experts average >= 384 rows, 192-token ones from 64 rows, 128-token
+    ones from 32, 64-token ones from 8, 16-token skinny tiles below; fp8
+    192-token stream tiles from 12 rows; bf16 tiles need widths that are
+    multiples of 64)."""
     R, E = cfg.T * cfg.topk, cfg.E
     if cfg.w_dtype == "fp8":
         return "moe::stream_fp8_kernel<true>" if R >= 12 * E else "moe::up_skinny_fp8_kernel"
     if cfg.w_dtype == "bf16" and cfg.dim % 64 == 0 and cfg.inter % 64 == 0 and cfg.inter_shared % 64 == 0:
         if R >= 384 * E:
             return "moe::stream_bf16_kernel<256-token tiles, up>"
-        if R >= 32 * E:
+        if R >= 64 * E:
             return "moe::stream_bf16_kernel<192-token tiles, up>"
+        if R >= 32 * E:
+            return "moe::stream_bf16_kernel<128-token tiles, up>"
         if R >= 8 * E:
             return "moe::stream_bf16_kernel<64-token tiles, up>"
     return "moe::up_skinny_kernel<%s>" % ("float" if cfg.w_dtype == "f32" else "unsigned short")
