@@ -266,11 +266,11 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 }
 
 // ---------------------------------------------------------------------------
-// Stream tiles (prefill): up to 192 token rows x 256 weight rows per
+// Stream tiles (prefill): 64 to 256 token rows x 256 weight rows per
 // workgroup of 8 waves (two per SIMD), on v_mfma_f32_32x32x16_bf16 (the
 // 32x32 shape runs at full rate on gfx950; 16x16x32 issues at half rate).
-// A tile covers a whole expert whenever it has <= 192 tokens, so each weight
-// slice is fetched from HBM once per expert.
+// A tile covers a whole expert whenever it has no more rows than the tile,
+// so each weight slice is fetched from HBM once per expert.
 //   A operand = 32 weight rows per wave, loaded straight from global memory
 //     through a ring of 4 register stages (three 64-element K slices in
 //     flight); for the up projection rows 0-15 are W1 rows and rows 16-31 the
@@ -1030,8 +1030,8 @@ enum class Tiles { Skinny, Mid, Big, Huge };
 // from batch-size sweeps on the DeepSeek-V3 shape): 16-token skinny tiles
 // below 8 rows (decode: weight streaming, each expert's weights read once);
 // from there every 16-token m-tile would re-read its expert's weights, so
-// stream tiles take over - 64-token tiles with three workgroups per CU below
-// 32 rows, whole-expert 192-token tiles up to 384 rows, 256-token tiles above
+// stream tiles take over - 64-token tiles below 32 rows, 128-token tiles
+// below 64, whole-expert 192-token tiles up to 384 rows, 256-token tiles above
 // (hot experts of many hundred rows).  fp8 weights switch to their 192-token
 // stream tiles from 12 rows.  Stream tiles need widths that are multiples of 64.
 static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
