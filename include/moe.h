@@ -90,7 +90,11 @@ typedef enum moe_accumulate {
  * Limits: 1 <= n_experts <= 512; n_experts % n_groups == 0; n_groups <= 64;
  *   1 <= topk_groups <= n_groups; 1 <= topk <= 32 and topk <= topk_groups *
  *   n_experts / n_groups; with a bias and n_groups > 1 each group needs >= 2
- *   experts; dim, inter and shared_inter multiples of 64 (of 128 for fp8).   */
+ *   experts; dim, inter and shared_inter multiples of 64 (of 128 for fp8)
+ *   and at most 65536; T < 2^24 tokens.  moe_expert_ffn and moe_forward also
+ *   return MOE_ERR_UNSUPPORTED, before enqueuing anything, when an expert
+ *   launch for T tokens would exceed the 2^32 - 1 work-items a dispatch can
+ *   count (only at extreme T x width products).                             */
 typedef struct moe_params {
   int32_t dim;           /* model width                                          */
   int32_t n_experts;     /* E, routed experts                                    */
@@ -212,7 +216,8 @@ moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
  * saturating to +-448; a zero result is code 0).  moe_expert_ffn applies it
  * to x and to h when weight_dtype is MOE_FP8_E4M3; it is exported so the
  * step can be used and checked on its own.
- *   x [rows, cols] bf16, cols a multiple of 128;
+ *   x [rows, cols] bf16, cols a multiple of 128, rows * cols / 128 <= 2^28 - 16
+ *   (MOE_ERR_UNSUPPORTED beyond);
  *   out q [rows, cols] e4m3fn codes; out scales [rows, cols/128] fp32. */
 moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
                          void* stream);

@@ -1009,7 +1009,6 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
 }
 
 static inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
-static inline int round8(long n) { return (int)((n + 7) / 8 * 8); }
 
 // Upper bound on the tiles of one projection: sum_g ceil(M_g / bm) <= R/bm + nonempty groups.
 static long max_tiles(long R, int E, int ntok, bool shared, int bm, int nt_routed, int nt_shared) {
@@ -1045,34 +1044,71 @@ static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
   return Tiles::Skinny;
 }
 
-hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
-  const bool has_shared = p.ws1 != nullptr && p.shared_out != nullptr && p.inter_s > 0;
+// Tile kind, tile sizes and grid sizes of the two projection launches.
+struct FfnPlan {
+  Tiles t;
+  bool nt;              // stream tiles read their weights non-temporally
+  int bm, nt_up, nt_up_s, nt_dn, threads;
+  long g_up, g_dn;      // workgroups (a multiple of 8)
+};
+
+static FfnPlan plan_ffn(const FfnProblem& p, bool has_shared) {
+  FfnPlan L{};
   const long R = (long)p.ntok * p.topk;
-  const Tiles t = pick_tiles(p, has_shared);
+  L.t = pick_tiles(p, has_shared);
   const bool f8 = p.wkind == WKind::FP8;
   // stream tiles read their weights non-temporally while experts average
   // fewer than 64 rows (one or two m-tiles each): measured faster there,
   // slower once the m-tiles of an expert share weight slices in L2
-  const bool nt = R < 64L * p.E;
-  int bm = 16, bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
-  if (t == Tiles::Big && f8) bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN;
-  else if (t == Tiles::Huge) bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN;
-  else if (t == Tiles::Big && nt) bm = SBigNT::BM, bn_up = SBigNT::UPBN, bn_dn = SBigNT::BN;
-  else if (t == Tiles::Big) bm = SBig::BM, bn_up = SBig::UPBN, bn_dn = SBig::BN;
-  else if (t == Tiles::Mid) bm = SMid::BM, bn_up = SMid::UPBN, bn_dn = SMid::BN;
-  const int nt_up = ceil_div(p.inter, bn_up), nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
-  const int nt_dn = ceil_div(p.dim, bn_dn);
-  ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.offsets, p.E, p.ntok, has_shared ? 1 : 0, bm, nt_up,
-                                          nt_up_s, bm, nt_dn, p.e_begin, p.e_end, p.sched);
+  L.nt = R < 64L * p.E;
+  int bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
+  L.bm = 16, L.threads = 256;
+  if (L.t == Tiles::Big && f8) L.bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN, L.threads = F8::THREADS;
+  else if (L.t == Tiles::Huge) L.bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN, L.threads = SHuge::THREADS;
+  else if (L.t == Tiles::Big && L.nt) L.bm = SBigNT::BM, bn_up = SBigNT::UPBN, bn_dn = SBigNT::BN, L.threads = SBigNT::THREADS;
+  else if (L.t == Tiles::Big) L.bm = SBig::BM, bn_up = SBig::UPBN, bn_dn = SBig::BN, L.threads = SBig::THREADS;
+  else if (L.t == Tiles::Mid) L.bm = SMid::BM, bn_up = SMid::UPBN, bn_dn = SMid::BN, L.threads = SMid::THREADS;
+  L.nt_up = ceil_div(p.inter, bn_up);
+  L.nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
+  L.nt_dn = ceil_div(p.dim, bn_dn);
+  L.g_up = (max_tiles(R, p.E, p.ntok, has_shared, L.bm, L.nt_up, L.nt_up_s) + 7) / 8 * 8;
+  L.g_dn = (max_tiles(R, p.E, p.ntok, has_shared, L.bm, L.nt_dn, L.nt_dn) + 7) / 8 * 8;
+  return L;
+}
+
+static long quant_blocks(int ntok, int dim) { return ((long)ntok * (dim / 128) * 16 + 255) / 256; }
+
+static long plan_items(const FfnProblem& p, const FfnPlan& L) {
+  long items = std::max(L.g_up, L.g_dn) * L.threads;
+  if (p.wkind == WKind::FP8) items = std::max(items, quant_blocks(p.ntok, p.dim) * 256);
+  return items;
+}
+
+long ffn_max_items(int ntok, int topk, int E, int dim, int inter, int inter_s, WKind wk,
+                   bool has_shared) {
+  FfnProblem p{};
+  p.ntok = ntok; p.topk = topk; p.E = E; p.dim = dim; p.inter = inter; p.inter_s = inter_s;
+  p.wkind = wk;
+  return plan_items(p, plan_ffn(p, has_shared && inter_s > 0));
+}
+
+hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
+  const bool has_shared = p.ws1 != nullptr && p.shared_out != nullptr && p.inter_s > 0;
+  const FfnPlan L = plan_ffn(p, has_shared);
+  // a launch counts its work-items in 32 bits; refuse before enqueuing anything
+  if (plan_items(p, L) > kMaxLaunchItems) return hipErrorInvalidConfiguration;
+  const Tiles t = L.t;
+  const bool f8 = p.wkind == WKind::FP8, nt = L.nt;
+  ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.offsets, p.E, p.ntok, has_shared ? 1 : 0, L.bm, L.nt_up,
+                                          L.nt_up_s, L.bm, L.nt_dn, p.e_begin, p.e_end, p.sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   FfnProblem q = p;
   if (!has_shared) { q.ws1 = q.ws3 = q.ws2 = nullptr; q.shared_out = nullptr; }
-  const int g_up = round8(max_tiles(R, p.E, p.ntok, has_shared, bm, nt_up, nt_up_s));
-  const int g_dn = round8(max_tiles(R, p.E, p.ntok, has_shared, bm, nt_dn, nt_dn));
+  const int g_up = (int)L.g_up, g_dn = (int)L.g_dn;
   auto mark = [&](int i) { if (p.ev[i]) (void)hipEventRecord(p.ev[i], st); };
   if (f8) {   // quantise x once (the 1x128 blocks do not depend on the expert)
-    quant_fp8_kernel<<<(int)(((long)p.ntok * (p.dim / 128) * 16 + 255) / 256), 256, 0, st>>>(
+    quant_fp8_kernel<<<(int)quant_blocks(p.ntok, p.dim), 256, 0, st>>>(
         static_cast<const uint16_t*>(p.x), p.ntok, p.dim, const_cast<uint8_t*>(p.xq),
         const_cast<float*>(p.xs));
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1105,7 +1141,8 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
 
 hipError_t launch_quant_x(const uint16_t* x, int rows, int cols, uint8_t* xq, float* xs,
                           hipStream_t st) {
-  quant_fp8_kernel<<<(int)(((long)rows * (cols / 128) * 16 + 255) / 256), 256, 0, st>>>(
+  if (quant_blocks(rows, cols) * 256 > kMaxLaunchItems) return hipErrorInvalidConfiguration;
+  quant_fp8_kernel<<<(int)quant_blocks(rows, cols), 256, 0, st>>>(
       x, rows, cols, xq, xs);
   return hipGetLastError();
 }

@@ -55,6 +55,11 @@ struct FfnProblem {
 
 size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool act_f32);
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t st);
+// A launch counts its work-items (workgroups x threads) in 32 bits.
+constexpr long kMaxLaunchItems = 0xFFFFFFFFL;
+// Work-items of the largest launch launch_ffn makes for these shapes (host only).
+long ffn_max_items(int ntok, int topk, int E, int dim, int inter, int inter_s, WKind wk,
+                   bool has_shared);
 hipError_t launch_quant_x(const uint16_t* x, int ntok, int dim, uint8_t* xq, float* xs,
                           hipStream_t st);
 

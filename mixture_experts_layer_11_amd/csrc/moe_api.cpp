@@ -57,6 +57,8 @@ struct Layout {
 
 size_t act_size(const moe_params* p) { return p->act_dtype == MOE_F32 ? 4 : 2; }
 
+constexpr int kMaxWidth = 65536;   // largest dim, inter and shared_inter
+
 WKind wkind(const moe_params* p) {
   return p->weight_dtype == MOE_FP8_E4M3 ? WKind::FP8
          : p->weight_dtype == MOE_BF16   ? WKind::BF16
@@ -96,7 +98,7 @@ Layout layout(const moe_params* p, int64_t T) {
 moe_status validate(const moe_params* p, int64_t T) {
   if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "params is NULL");
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
-  if (T > (int64_t)1 << 24) return fail(MOE_ERR_UNSUPPORTED, "T > 2^24 tokens");
+  if (T >= (int64_t)1 << 24) return fail(MOE_ERR_UNSUPPORTED, "T >= 2^24 tokens");
   const int E = p->n_experts, G = p->n_groups;
   if (E < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts < 1");
   if (E > moe::kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > 512");
@@ -116,6 +118,8 @@ moe_status validate(const moe_params* p, int64_t T) {
     return fail(MOE_ERR_INVALID_ARG, "expert range must satisfy 0 <= expert_begin <= expert_end <= n_experts");
   if (p->dim < 1 || p->inter < 1 || p->shared_inter < 0)
     return fail(MOE_ERR_INVALID_ARG, "dim and inter must be >= 1, shared_inter >= 0");
+  if (p->dim > kMaxWidth || p->inter > kMaxWidth || p->shared_inter > kMaxWidth)
+    return fail(MOE_ERR_UNSUPPORTED, "dim, inter and shared_inter must be <= 65536");
   const bool f32 = p->act_dtype == MOE_F32 && p->router_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
   const bool bf = p->act_dtype == MOE_BF16 && p->router_dtype == MOE_BF16 &&
                   (p->weight_dtype == MOE_BF16 || p->weight_dtype == MOE_FP8_E4M3);
@@ -124,6 +128,15 @@ moe_status validate(const moe_params* p, int64_t T) {
   if (p->dim % q || p->inter % q || p->shared_inter % q)
     return fail(MOE_ERR_UNSUPPORTED, q == 128 ? "dim, inter, shared_inter must be multiples of 128 for fp8"
                                               : "dim, inter, shared_inter must be multiples of 64");
+  return MOE_OK;
+}
+
+// Every launch of the expert step must fit a dispatch's 32-bit work-item count.
+moe_status check_launch_size(const moe_params* p, int64_t T, bool shared) {
+  const long items = moe::ffn_max_items((int)T, p->topk, p->n_experts, p->dim, p->inter,
+                                        p->shared_inter, wkind(p), shared);
+  if (items > moe::kMaxLaunchItems)
+    return fail(MOE_ERR_UNSUPPORTED, "T and the widths give an expert launch of more than 2^32 - 1 work-items");
   return MOE_OK;
 }
 
@@ -322,6 +335,7 @@ moe_status moe_expert_ffn(const moe_params* p, int64_t T, const void* x,
   if (s != MOE_OK) return s;
   if (shared_out != nullptr && p->shared_inter == 0)
     return fail(MOE_ERR_INVALID_ARG, "shared_out must be NULL when shared_inter = 0");
+  if ((s = check_launch_size(p, T, shared_out != nullptr)) != MOE_OK) return s;
   if ((s = check_weights(p, w, false, shared_out != nullptr)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!x || !sorted_token || !offsets || !expert_out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
@@ -351,7 +365,9 @@ moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, 
   g_err.clear();
   if (rows < 0 || cols < 128 || cols % 128 != 0)
     return fail(MOE_ERR_INVALID_ARG, "rows >= 0 and cols a positive multiple of 128 required");
-  if (rows > ((int64_t)1 << 31) / (cols / 128)) return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
+  // 16 work-items per 1x128 block; a dispatch counts at most 2^32 - 1
+  if (rows > (((int64_t)1 << 28) - 16) / (cols / 128))
+    return fail(MOE_ERR_UNSUPPORTED, "rows * cols / 128 must be <= 2^28 - 16");
   if (rows == 0) return MOE_OK;
   if (!x || !q || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
   hipError_t e = moe::launch_quant_x(static_cast<const uint16_t*>(x), (int)rows, cols, q, scales,
@@ -388,6 +404,7 @@ moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_
   if (s != MOE_OK) return s;
   if ((s = check_weights(p, w, true, true)) != MOE_OK) return s;
   if ((s = bias_rule(p, w->bias)) != MOE_OK) return s;
+  if ((s = check_launch_size(p, T, p->shared_inter > 0)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
   if ((s = check_ws(p, T, workspace, workspace_bytes)) != MOE_OK) return s;

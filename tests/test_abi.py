@@ -67,11 +67,55 @@ def _ws_status(p, T=16):
     (dict(act_dtype="f32"), moe.MOE_ERR_UNSUPPORTED),        # mixed dtypes
     (dict(weight_dtype="fp8", inter=2000), moe.MOE_ERR_UNSUPPORTED),
     (dict(topk=40, topk_groups=8), moe.MOE_ERR_UNSUPPORTED),  # topk > 32
+    (dict(dim=65600), moe.MOE_ERR_UNSUPPORTED),              # wider than 65536
+    (dict(inter=65600), moe.MOE_ERR_UNSUPPORTED),
+    (dict(shared_inter=65600), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_params_rejected_on_host(kw, status):
     s, _ = _ws_status(_p(**kw))
     assert s == status
     assert moe.lib().moe_last_error().decode() != ""
+
+
+def test_token_count_limit():
+    # the combine runs one 256-thread workgroup per token: 2^24 of them would
+    # need 2^32 work-items, one more than a dispatch counts
+    assert _ws_status(_p(), (1 << 24) - 1)[0] == moe.MOE_OK
+    assert _ws_status(_p(), 1 << 24)[0] == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_oversized_expert_launch_rejected_before_enqueue():
+    # 8 experts of 2^21 rows each on 256-token tiles, 512 column tiles of a
+    # 65536-wide expert: far beyond 2^32 work-items.  The pointers are never
+    # dereferenced because the call returns first.
+    p = _p(n_experts=8, n_groups=1, topk_groups=1, topk=8, dim=64, inter=65536,
+           shared_inter=65536)
+    fake = ctypes.c_void_p(256)
+    w = moe.moe_weights(w_router=256, w1=256, w3=256, w2=256, ws1=256, ws3=256, ws2=256)
+    L = moe.lib()
+    T = (1 << 24) - 1
+    assert _ws_status(p, T)[0] == moe.MOE_OK          # the shapes themselves are valid
+    s = L.moe_expert_ffn(ctypes.byref(p.c()), T, fake, fake, fake, ctypes.byref(w), fake,
+                         fake, fake, 1 << 62, None)
+    assert s == moe.MOE_ERR_UNSUPPORTED and "work-items" in L.moe_last_error().decode()
+    s = L.moe_forward(ctypes.byref(p.c()), T, fake, ctypes.byref(w), fake, None, None, None,
+                      fake, 1 << 62, None)
+    assert s == moe.MOE_ERR_UNSUPPORTED and "work-items" in L.moe_last_error().decode()
+    # a decode-sized batch of the same layer passes the check and stops at the
+    # (deliberately too small) workspace instead
+    s = L.moe_expert_ffn(ctypes.byref(p.c()), 16, fake, fake, fake, ctypes.byref(w), fake,
+                         fake, fake, 16, None)
+    assert s == moe.MOE_ERR_WORKSPACE
+
+
+def test_quant_fp8_block_limit():
+    fake = ctypes.c_void_p(256)
+    L = moe.lib()
+    # 16 work-items per block, rounded up to 256-thread workgroups
+    assert L.moe_quant_fp8(fake, (1 << 28) - 15, 128, fake, fake, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_fp8(fake, 1 << 25, 1024, fake, fake, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quant_fp8(fake, 100, 100, fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quant_fp8(fake, 0, 128, fake, fake, None) == moe.MOE_OK
 
 
 def test_unknown_accumulate_mode_rejected():
