@@ -180,9 +180,11 @@ template <> __device__ __forceinline__ void store4<float>(float* p, const float 
 
 constexpr int kSkinnyWaves = 4;
 constexpr int kUpNT = 2;     // 16-row tiles of W1 (and of W3) per wave
-constexpr int kDnNT = 4;     // 16-row tiles of W2 per wave
+constexpr int kDnNT = 2;     // 16-row tiles of W2 per wave (bf16, fp32)
+constexpr int kDnNT8 = 4;    // 16-row tiles of W2 per wave (fp8)
 constexpr int kUpBN = kSkinnyWaves * 16 * kUpNT;   // h columns per workgroup
 constexpr int kDnBN = kSkinnyWaves * 16 * kDnNT;   // output columns per workgroup
+constexpr int kDnBN8 = kSkinnyWaves * 16 * kDnNT8;
 
 template <typename T>
 __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
@@ -951,7 +953,7 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   const int N = p.dim;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
-  const int nbase = ti.nt * kDnBN + wave * 16 * kDnNT;
+  const int nbase = ti.nt * kDnBN8 + wave * 16 * kDnNT8;
   if (nbase >= N) return;
   const int mi = ti.m0 + min(r, ti.mrows - 1);
   const size_t hrow = shared ? (size_t)mi : (size_t)(ti.row0 + mi);
@@ -959,21 +961,21 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   const float* bsc = (shared ? p.hsscale : p.hscale) + hrow * KB;
   const uint8_t* W2 = static_cast<const uint8_t*>(shared ? p.ws2 : p.w2) + (shared ? 0 : (size_t)(ti.g - p.e_begin) * N * K);
   const float* S2 = (shared ? p.ws2s : p.w2s + (size_t)(ti.g - p.e_begin) * (N / 128) * KB);
-  const char* ap[kDnNT];
-  const float* sp[kDnNT];
+  const char* ap[kDnNT8];
+  const float* sp[kDnNT8];
 #pragma unroll
-  for (int j = 0; j < kDnNT; ++j) {
+  for (int j = 0; j < kDnNT8; ++j) {
     const int n = nbase + 16 * j;
     ap[j] = reinterpret_cast<const char*>(W2) + wtile_off(n + r, 32 * grp, K);
     sp[j] = S2 + (size_t)(n / 128) * KB;
   }
-  f32x4_t acc[kDnNT];
+  f32x4_t acc[kDnNT8];
 #pragma unroll
-  for (int j = 0; j < kDnNT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 a[2][kDnNT][2], b[2][2];
+  for (int j = 0; j < kDnNT8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 a[2][kDnNT8][2], b[2][2];
   auto load = [&](int s, int kb) {
 #pragma unroll
-    for (int j = 0; j < kDnNT; ++j) {
+    for (int j = 0; j < kDnNT8; ++j) {
       a[s][j][0] = ldg16_stream(ap[j] + 2 * kChunkStride * kb);
       a[s][j][1] = ldg16_stream(ap[j] + 2 * kChunkStride * kb + 256);
     }
@@ -983,7 +985,7 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   auto comp = [&](int s, int kb) {
     const float hsc = bsc[kb];
 #pragma unroll
-    for (int j = 0; j < kDnNT; ++j) {
+    for (int j = 0; j < kDnNT8; ++j) {
       const f32x4_t part = mma_fp8(a[s][j][0], a[s][j][1], b[s][0], b[s][1]);
       const float sc = sp[j][kb] * hsc;
 #pragma unroll
@@ -1001,7 +1003,7 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   if (r < ti.mrows) {
     uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) + (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
 #pragma unroll
-    for (int j = 0; j < kDnNT; ++j) {
+    for (int j = 0; j < kDnNT8; ++j) {
       float v[4] = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
       store4<uint16_t>(orow + nbase + 16 * j + 4 * grp, v);
     }
@@ -1061,7 +1063,7 @@ static FfnPlan plan_ffn(const FfnProblem& p, bool has_shared) {
   // fewer than 64 rows (one or two m-tiles each): measured faster there,
   // slower once the m-tiles of an expert share weight slices in L2
   L.nt = R < 64L * p.E;
-  int bn_up = kUpBN, bn_dn = kDnBN;   // skinny tiles
+  int bn_up = kUpBN, bn_dn = p.wkind == WKind::FP8 ? kDnBN8 : kDnBN;   // skinny tiles
   L.bm = 16, L.threads = 256;
   if (L.t == Tiles::Big && f8) L.bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN, L.threads = F8::THREADS;
   else if (L.t == Tiles::Huge) L.bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN, L.threads = SHuge::THREADS;
