@@ -185,6 +185,7 @@ constexpr int kDnNT8 = 4;    // 16-row tiles of W2 per wave (fp8)
 constexpr int kUpBN = kSkinnyWaves * 16 * kUpNT;   // h columns per workgroup
 constexpr int kDnBN = kSkinnyWaves * 16 * kDnNT;   // output columns per workgroup
 constexpr int kDnBN8 = kSkinnyWaves * 16 * kDnNT8;
+static_assert(kUpBN == 128, "the fp8 decode up kernel covers 128 h columns per workgroup");
 
 template <typename T>
 __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
