@@ -257,8 +257,12 @@ def cpu_baseline(layer, ntok):
                        E=cfg.E, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, topk=cfg.topk,
                        score_func=cfg.score_func, route_scale=cfg.route_scale)
     dt = time.perf_counter() - t
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    host = len(os.sched_getaffinity(0))
+    ram = os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES")
+    # the oracle's parallel work is its BLAS calls: it runs on min(BLAS threads, cores) cores
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(min(blas, host)), "kind": "oracle",
+            "host_cores": host, "blas_threads": int(blas), "host_ram_GB": round(ram / 1e9, 1),
             "sample": f"first {ntok} of the {cfg.T} tokens of {cfg.name} (gate, their routed "
                       f"experts and the shared expert), {dt:.1f} s"}
 

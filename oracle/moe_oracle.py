@@ -9,8 +9,9 @@ Sources (web pages; cited by title and section):
             dtype note (router held in bf16, applied in fp32), the Gate
             constructor and Gate.forward code excerpts, the summary sentences.
   [combine] "DeepSeek-V3.2-Exp · Weighted expert sum" - formula
-            y_routed = sum_i G_i E_i, "accumulated in float32 and cast back at
-            the end", the MoE.forward code excerpt and its summary sentence.
+            y_routed = sum_i G_i E_i, the note that the sum is kept in fp32
+            and converted to the input dtype once at the end, the MoE.forward
+            code excerpt and its summary sentence.
   [v3]      hackaday.io log "Time to jump right in and swim with the big fish"
             - the original DeepSeek-V3 MoE class (constructor: Expert(dim,
             moe_inter_dim), MLP(dim, n_shared_experts*moe_inter_dim)).
@@ -36,11 +37,12 @@ also listed in the design notes):
   R5 softmax weights are not renormalised (only sigmoid is).
   R6 the shared expert is one MLP of inner width n_shared * inter.
   R9 the accumulator is fp32 by default ([combine]); the original V3 class
-     ([v3], MoE.forward: y = zeros_like(x), y[idx] += expert(x[idx]) *
-     weights per expert in ascending id, return y + z) is the second mode
-     ("layer"): the running sum lives in the layer dtype, each update is
-     computed in fp32 (a bf16 tensor times fp32 weights promotes to fp32) and
-     cast back, and the shared output is added last with one more cast.
+     ([v3], its MoE.forward) is the second mode ("layer"): the running sum
+     starts at zero in the layer dtype, the routed experts are visited in
+     ascending id and each adds its weighted outputs to its tokens' rows, the
+     update evaluated in fp32 (a bf16 tensor times fp32 weights promotes) and
+     stored back in the layer dtype; the shared output is added last, with
+     one more cast.
 """
 
 from __future__ import annotations
@@ -314,7 +316,8 @@ def brute_force_select(s, bias, n_groups, topk_groups, topk):
 
 
 # ---------------------------------------------------------------------------
-# dispatch  ([combine]: bincount, per-expert torch.where in row-major order)
+# dispatch  ([combine]: a count per expert, then each expert's (token, slot)
+#            pairs in row-major order)
 # ---------------------------------------------------------------------------
 
 
@@ -323,7 +326,7 @@ def permute(idx: np.ndarray, E: int):
 
     counts[e] = number of assignments to e; offsets = exclusive prefix sum;
     inside expert e's segment the tokens appear in ascending order (the order
-    torch.where(indices == e) yields); row_of[t, k] is the position of
+    a row-major search of the index matrix yields); row_of[t, k] is the position of
     assignment (t, k).  Returns int32 arrays.
     """
     T, K = idx.shape

@@ -347,25 +347,33 @@ def test_fp8_expert_close_to_unquantised():
 # layer-dtype accumulator ([v3] MoE.forward; reading R9)
 # ---------------------------------------------------------------------------
 
-def _v3_statements_in_torch(outs, w, idx, shared, dtype):
-    """The original V3 class's combine run with torch on the CPU, statement by
-    statement: y = zeros_like(x); per expert in ascending id,
-    idx, top = where(indices == i); y[idx] += expert(x[idx]) * weights[idx, top, None];
-    then y + z.  The expert outputs are given (outs[t, k] = expert idx[t,k] of t)."""
+def _v3_combine_in_torch(outs, w, idx, shared, dtype):
+    """The V3 class's combine (hackaday.io log, MoE.forward), written with torch
+    on the CPU from its definition: an expert-contiguous permutation of the
+    (token, slot) pairs (a stable sort of the expert ids), then for each
+    expert in ascending id one vectorised update of its tokens' rows - the
+    running sum, held in the layer dtype, plus output times weight, evaluated
+    in fp32 by torch's type promotion and stored back in the layer dtype - and
+    finally the shared output added with torch's own bf16 addition."""
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     T, K, dim = outs.shape
-    outs_t = torch.from_numpy(outs.astype(np.float32)).to(tdt)      # exact: values are layer dtype
-    weights = torch.from_numpy(w.astype(np.float32))
-    indices = torch.from_numpy(idx.astype(np.int64))
+    o = torch.from_numpy(outs.astype(np.float32)).to(tdt)        # exact: values are layer dtype
+    wt = torch.from_numpy(w.astype(np.float32))
+    ids = torch.from_numpy(idx.astype(np.int64)).reshape(-1)
+    perm = torch.sort(ids, stable=True).indices                  # expert-contiguous pairs
+    counts = torch.bincount(ids, minlength=int(ids.max()) + 1).tolist()
     y = torch.zeros((T, dim), dtype=tdt)
-    for i in range(int(idx.max()) + 1):
-        rows, top = torch.where(indices == i)
-        if rows.numel() == 0:
+    start = 0
+    for c in counts:
+        seg = perm[start:start + c]
+        start += c
+        if c == 0:
             continue
-        y[rows] += outs_t[rows, top] * weights[rows, top, None]
+        tok, slot = seg // K, seg % K
+        y[tok] = (y[tok] + o[tok, slot] * wt[tok, slot].unsqueeze(1)).to(tdt)
     z = torch.from_numpy(shared.astype(np.float32)).to(tdt)
-    return (y + z).float().numpy().astype(np.float64)
+    return torch.add(y, z).float().numpy().astype(np.float64)
 
 
 def check_combine_layer_matches_torch(dtype="bf16", seed=3):
@@ -377,7 +385,7 @@ def check_combine_layer_matches_torch(dtype="bf16", seed=3):
     outs = oracle.round_to(raw, dtype)
     shared = oracle.round_to(rng.standard_normal((T, dim)), dtype)
     got = oracle.combine_layer(outs, w, idx, shared, dtype)
-    ref = _v3_statements_in_torch(outs, w, idx, shared, dtype)
+    ref = _v3_combine_in_torch(outs, w, idx, shared, dtype)
     np.testing.assert_array_equal(got, ref)
     return got
 

@@ -149,3 +149,76 @@ def test_layer_combine_in_slot_order_is_caught(monkeypatch):
     _patch(monkeypatch, "combine_layer", slot_order)
     with pytest.raises(AssertionError):
         pins.check_combine_layer_matches_torch("bf16")
+
+
+# ---------------------------------------------------------------------------
+# fp8 expert path: three plausible quantisation mistakes
+# ---------------------------------------------------------------------------
+
+def _quant_along_tokens(h):
+    """Mistake: one scale per column over blocks of 128 token rows."""
+    M, K = h.shape
+    pad = (-M) % 128
+    ht = np.pad(np.asarray(h, F32).T, ((0, 0), (0, pad)))
+    return mo.quantize_act_1x128(ht)[2][:, :M].T
+
+
+def _fp8_ffn_with(mistake):
+    orig = mo.expert_ffn
+
+    def ffn(xv, w1, w3, w2, w_dtype, act_dtype, w1_s=None, w3_s=None, w2_s=None, xq=None):
+        if w_dtype != "fp8":
+            return orig(xv, w1, w3, w2, w_dtype, act_dtype, w1_s, w3_s, w2_s, xq)
+        W1 = mo.decode_weights(w1, "fp8", w1_s)
+        W3 = mo.decode_weights(w3, "fp8", w3_s)
+        W2 = mo.decode_weights(w2, "fp8", w2_s)
+        if mistake == "x_unquantised":
+            xin = np.asarray(xv, np.float64)
+        else:
+            xin = xq if xq is not None else mo.quantize_act_1x128(xv)[2]
+        h32 = mo.swiglu(xin @ W1.T, xin @ W3.T).astype(F32)
+        if mistake == "h_unquantised":
+            hin = h32.astype(np.float64)
+        elif mistake == "h_along_tokens":
+            hin = _quant_along_tokens(h32)
+        else:
+            hin = mo.quantize_act_1x128(h32)[2]
+        return mo.round_to(hin @ W2.T, act_dtype)
+    return ffn
+
+
+FP8_MISTAKES = ["h_unquantised", "h_along_tokens", "x_unquantised"]
+
+
+@pytest.mark.parametrize("mistake", FP8_MISTAKES)
+def test_fp8_hand_example_catches(mistake, monkeypatch):
+    from tests import test_oracle_fp8 as fp8pins
+    _patch(monkeypatch, "expert_ffn", _fp8_ffn_with(mistake))
+    with pytest.raises(AssertionError):
+        fp8pins.check_fp8_hand_example()
+
+
+@pytest.mark.parametrize("mistake", ["h_unquantised", "h_along_tokens"])
+def test_fp8_block_grid_catches(mistake, monkeypatch):
+    from tests import test_oracle_fp8 as fp8pins
+    _patch(monkeypatch, "expert_ffn", _fp8_ffn_with(mistake))
+    with pytest.raises(AssertionError):
+        fp8pins.check_fp8_h_on_block_grid()
+
+
+@pytest.mark.parametrize("cfg_name", ["s3_mini_fp8", "s7_mini_fp8_decode"])
+@pytest.mark.parametrize("mistake", FP8_MISTAKES)
+def test_fp8_layer_bar_rejects(cfg_name, mistake, monkeypatch):
+    """The GPU parity bar for fp8 layers must not admit any of the mistakes:
+    the layer output of a mutated oracle, compared with the oracle's own, lies
+    outside the bar (on a token subset, to keep the CPU time small)."""
+    from mixture_experts_layer_11_amd import inputs
+    from tests.helpers import FP8_BAR, rel_errors, run_oracle
+    layer = inputs.draw_layer(inputs.config_by_name(cfg_name))
+    tok = np.arange(0, layer.cfg.T, 3)
+    good = run_oracle(layer, tokens=tok)
+    monkeypatch.setattr(mo, "expert_ffn", _fp8_ffn_with(mistake))
+    bad = run_oracle(layer, tokens=tok)
+    np.testing.assert_array_equal(good["idx"], bad["idx"])     # the gate is untouched
+    mx, mean = rel_errors(bad["y"], good["y"])
+    assert mean > FP8_BAR[1], (mistake, mx, mean)
