@@ -66,14 +66,14 @@ typedef enum moe_score {
  *                 y starts as fp32 zeros): y_t = cast( sum_k w O + S ), fp32
  *                 throughout, one cast at the end.
  *   MOE_ACC_LAYER (the original DeepSeek-V3 MoE.forward in the hackaday.io log
- *                 "Time to jump right in and swim with the big fish": y starts
- *                 as zeros of x's dtype, experts are visited in ascending id and
- *                 each does y[idx] += expert(x[idx]) * weights, then y + z with
- *                 the shared output z): y_t = 0 in the layer dtype; for each of
- *                 the token's experts in ascending id, y_t = cast(y_t + O*w)
- *                 with the product and the sum in fp32 (torch's promotion of a
- *                 bf16 tensor times fp32 weights); finally y_t = cast(y_t + S_t).
- *                 With fp32 layers every cast is the identity.               */
+ *                 "Time to jump right in and swim with the big fish": the
+ *                 running sum lives in x's dtype, the routed experts add their
+ *                 weighted outputs in ascending id, the shared output last):
+ *                 y_t = 0 in the layer dtype; for each of the token's experts
+ *                 in ascending id, y_t = cast(y_t + O*w) with the product and
+ *                 the sum in fp32 (torch's promotion of a bf16 tensor times
+ *                 fp32 weights); finally y_t = cast(y_t + S_t).  With fp32
+ *                 layers every cast is the identity.                         */
 typedef enum moe_accumulate {
   MOE_ACC_F32 = 0,
   MOE_ACC_LAYER = 1
@@ -91,7 +91,7 @@ typedef enum moe_accumulate {
  *   1 <= topk_groups <= n_groups; 1 <= topk <= 32 and topk <= topk_groups *
  *   n_experts / n_groups; with a bias and n_groups > 1 each group needs >= 2
  *   experts; dim, inter and shared_inter multiples of 64 (of 128 for fp8)
- *   and at most 65536; T < 2^24 tokens.  moe_expert_ffn and moe_forward also
+ *   and at most 65536; T < 2^24 tokens.  moe_expert_ffn, moe_combine and moe_forward also
  *   return MOE_ERR_UNSUPPORTED, before enqueuing anything, when an expert
  *   launch for T tokens would exceed the 2^32 - 1 work-items a dispatch can
  *   count (only at extreme T x width products).                             */
@@ -132,7 +132,10 @@ typedef struct moe_params {
  * logical ones and the byte sizes are unchanged.
  * fp8 scales: one fp32 per 128x128 block, [out/128, in/128] per matrix,
  * row-major, stacked over experts for the routed ones; NULL unless
- * weight_dtype is fp8. */
+ * weight_dtype is fp8.  Each scale must be a positive normal float (what the
+ * amax/448 quantiser produces, 1.0 for an all-zero block); the library reads
+ * them only on the device and does not check them, so a zero, subnormal,
+ * negative or non-finite scale gives undefined results. */
 typedef struct moe_weights {
   const void* w_router;   /* [E, dim], router_dtype                             */
   const float* bias;      /* [E] fp32 selection bias, or NULL for none          */
@@ -180,35 +183,44 @@ moe_status moe_permute(const moe_params* p, int64_t T, const int32_t* topk_idx,
                        int32_t* row_of, void* workspace, size_t workspace_bytes,
                        void* stream);
 
-/* Experts (SwiGLU; MoE constructor: Expert(dim, moe_inter_dim) per routed
- * expert, MLP(dim, n_shared_experts * moe_inter_dim) shared).
+/* Routed experts (SwiGLU; MoE constructor: Expert(dim, moe_inter_dim) per
+ * routed expert).
  *   x [T, dim]; sorted_token and offsets as produced by moe_permute (read on
- *   the device: no host synchronisation on the per-expert counts).
+ *   the device: no host synchronisation on the per-expert counts); w: the
+ *   routed weights w1, w3, w2 (and scales) are used.
  *   out expert_out [T*topk, dim] act_dtype: row r = FFN_e(x[sorted_token[r]])
- *       for the expert e whose segment holds r;
- *   out shared_out [T, dim] act_dtype: FFN_shared(x_t); may be NULL (then the
- *       shared expert is skipped) and must be NULL when shared_inter = 0.
+ *       for the expert e whose segment holds r (rows of experts outside the
+ *       expert range are left untouched).
  *   SwiGLU pre-activations are fp32; h = silu(a1)*a3 is rounded once (bf16,
  *   fp32, or e4m3 per 1x128 block for fp8 weights, where x is quantised the
  *   same way); outputs are rounded to act_dtype. */
 moe_status moe_expert_ffn(const moe_params* p, int64_t T, const void* x,
                           const int32_t* sorted_token, const int32_t* offsets,
-                          const moe_weights* w, void* expert_out, void* shared_out,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          const moe_weights* w, void* expert_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
-/* Combine ("Weighted expert sum": y[idx] += expert(x[idx]) * weights, fp32
- * accumulator, shared expert added, cast back at the end).
- *   expert_out [T*topk, dim] act_dtype; row_of [T, topk]; topk_w [T, topk] fp32;
- *   shared_out [T, dim] or NULL.
+/* Shared expert and combine ("Weighted expert sum": the weighted routed
+ * outputs summed in fp32, the shared expert's output added, one cast back at
+ * the end; the shared expert is the MoE constructor's MLP(dim,
+ * n_shared_experts * moe_inter_dim)).
+ *   x [T, dim] act_dtype (the shared expert's input; may be NULL when
+ *   shared_inter = 0); expert_out [T*topk, dim] act_dtype; row_of [T, topk];
+ *   topk_w [T, topk] fp32; w: the shared weights ws1, ws3, ws2 (and scales)
+ *   are used when shared_inter > 0.
  *   out y [T, dim] act_dtype = cast(sum_k topk_w[t,k] * expert_out[row_of[t,k]]
- *       + shared_out[t]); the k sum visits the token's experts in ascending id
+ *       + S_t) with S = FFN_shared(x) rounded to act_dtype (h rounded as in
+ *       moe_expert_ffn); the k sum visits the token's experts in ascending id
  *       (ascending row, since rows are expert-contiguous; a token's rows must be
- *       distinct) and adds the shared output last; each product and each sum
- *       is rounded to fp32 (no fused multiply-add); MOE_ACC_LAYER also casts the
- *       running sum to act_dtype after every addition. */
-moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
-                       const int32_t* row_of, const float* topk_w, const void* shared_out,
-                       void* y, void* stream);
+ *       distinct) and adds S last; each product and each sum is rounded to
+ *       fp32 (no fused multiply-add); MOE_ACC_LAYER also casts the running sum
+ *       to act_dtype after every addition.
+ *   With a shared expert and topk <= 8 the sum is formed in the epilogue of
+ *   the shared expert's down projection (S never leaves the chip); otherwise
+ *   S goes through the workspace to a separate combine kernel.  Same result
+ *   either way.  Needs the full expert range. */
+moe_status moe_combine(const moe_params* p, int64_t T, const void* x, const void* expert_out,
+                       const int32_t* row_of, const float* topk_w, const moe_weights* w,
+                       void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* fp8 activation quantiser (the block scheme of fp8 experts: each row split
  * into 1x128 blocks; scale = amax / 448, or 1 when the block is all zero;
@@ -274,7 +286,7 @@ const char* moe_last_error(void);
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t moe_abi_version(void);
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

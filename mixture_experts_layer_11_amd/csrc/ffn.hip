@@ -25,41 +25,44 @@
 
 namespace moe {
 
+// Three schedules of E + 2 ints each: the up launch, the down launch, and the
+// down launch of the shared expert fused with the combine.  Entry g is the
+// first tile of group g, entry E + 1 the launch's tile count.
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets,
-                                                            int E, int ntok, int has_shared,
-                                                            int bm_up, int nt_up, int nt_up_s,
-                                                            int bm_dn, int nt_dn, int e_begin,
-                                                            int e_end,
+                                                            int E, int ntok, int routed,
+                                                            int shared_up, int shared_down,
+                                                            int bm, int nt_up, int nt_up_s,
+                                                            int nt_dn, int e_begin, int e_end,
                                                             int32_t* __restrict__ sched) {
-  __shared__ int su[1024], sd[1024];
+  __shared__ int sc[3][1024];
   const int g = threadIdx.x;
-  int cu = 0, cd = 0;
-  if (g < E && g >= e_begin && g < e_end) {   // experts outside the range get no tiles
-    const int M = offsets[g + 1] - offsets[g];
-    cu = (M + bm_up - 1) / bm_up * nt_up;
-    cd = (M + bm_dn - 1) / bm_dn * nt_dn;
-  } else if (g == E && has_shared) {
-    cu = (ntok + bm_up - 1) / bm_up * nt_up_s;
-    cd = (ntok + bm_dn - 1) / bm_dn * nt_dn;
+  int c[3] = {0, 0, 0};
+  if (routed && g < E && g >= e_begin && g < e_end) {   // experts outside the range get no tiles
+    const int mt = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
+    c[0] = mt * nt_up;
+    c[1] = mt * nt_dn;
+  } else if (g == E) {
+    const int mt = (ntok + bm - 1) / bm;
+    c[0] = shared_up ? mt * nt_up_s : 0;
+    c[1] = shared_down == 1 ? mt * nt_dn : 0;
+    c[2] = shared_down == 2 ? mt * nt_dn : 0;
   }
-  su[g] = cu;
-  sd[g] = cd;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) sc[s][g] = c[s];
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    const int vu = g >= o ? su[g - o] : 0;
-    const int vd = g >= o ? sd[g - o] : 0;
+    int v[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) v[s] = g >= o ? sc[s][g - o] : 0;
     __syncthreads();
-    su[g] += vu;
-    sd[g] += vd;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) sc[s][g] += v[s];
     __syncthreads();
   }
-  if (g <= E) {
-    sched[g] = su[g] - cu;
-    sched[E + 2 + g] = sd[g] - cd;
-  }
-  if (g == E) {
-    sched[E + 1] = su[g];
-    sched[E + 2 + E + 1] = sd[g];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (g <= E) sched[s * (E + 2) + g] = sc[s][g] - c[s];
+    if (g == E) sched[s * (E + 2) + E + 1] = sc[s][g];
   }
 }
 
@@ -230,10 +233,27 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
   }
 }
 
+// The fused combine of a shared-expert down tile: the tile's outputs go to
+// LDS rounded to the layer dtype (the shared module's output), then the whole
+// workgroup forms y for the tile's tokens and columns (combine.h).
 template <typename T>
+__device__ __forceinline__ void combine_from_lds(const FfnProblem& p, const T* s_tile, int ld,
+                                                 const TileInfo& ti, int n0, int bn) {
+  const int ncols = min(bn, p.dim - n0);
+  if (p.comb.layer_acc)
+    combine_tile<T, true>(p.comb, s_tile, ld, ti.m0, ti.mrows, n0, ncols, p.dim);
+  else
+    combine_tile<T, false>(p.comb, s_tile, ld, ti.m0, ti.mrows, n0, ncols, p.dim);
+}
+
+// kComb: the launch holds only the shared expert's tiles, and each ends with
+// the combine instead of storing the shared output.
+template <typename T, bool kComb>
 __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
+  constexpr int LD = kDnBN + 8;                     // LDS row of the combine tile (elements)
+  __shared__ __attribute__((aligned(16))) T s_tile[kComb ? 16 * LD : 1];
   TileInfo ti;
-  const int32_t* sched = p.sched + p.E + 2;
+  const int32_t* sched = p.sched + (kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, ti)) return;
   const bool shared = ti.g == p.E;
   const int K = shared ? p.inter_s : p.inter;
@@ -241,7 +261,8 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int nbase = ti.nt * kDnBN + wave * 16 * kDnNT;
-  if (nbase >= N) return;
+  if (!kComb && nbase >= N) return;
+  const bool active = nbase < N;                    // waves past the last column still meet the barrier
   const int mi = ti.m0 + min(r, ti.mrows - 1);
   const T* hrow = shared ? static_cast<const T*>(p.hs) + (size_t)mi * K
                          : static_cast<const T*>(p.h) + (size_t)(ti.row0 + mi) * K;
@@ -250,13 +271,29 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   const char* ap[kDnNT];
 #pragma unroll
   for (int j = 0; j < kDnNT; ++j)
-    ap[j] = reinterpret_cast<const char*>(W2) + wtile_off(nbase + 16 * j + r, 16 * grp, K * (int)sizeof(T));
+    ap[j] = reinterpret_cast<const char*>(W2) + wtile_off(min(nbase + 16 * j + r, N - 1), 16 * grp, K * (int)sizeof(T));
   f32x4_t acc[kDnNT];
 #pragma unroll
   for (int j = 0; j < kDnNT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  kloop<T, kDnNT, 2>(ap, bp, K * (int)sizeof(T) / 64, acc);
+  if (active) kloop<T, kDnNT, 2>(ap, bp, K * (int)sizeof(T) / 64, acc);
 
   const int m = ti.m0 + r;
+  if constexpr (kComb) {
+    if (active && r < ti.mrows) {
+#pragma unroll
+      for (int j = 0; j < kDnNT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = to_layer<T>(acc[j][i]);
+          T* d = s_tile + r * LD + wave * 16 * kDnNT + 16 * j + 4 * grp + i;
+          if constexpr (sizeof(T) == 2) *d = (T)(__float_as_uint(v) >> 16);
+          else *d = v;
+        }
+    }
+    __syncthreads();
+    combine_from_lds<T>(p, s_tile, LD, ti, ti.nt * kDnBN, kDnBN);
+    return;
+  }
   if (r < ti.mrows) {
     T* orow = shared ? static_cast<T*>(p.shared_out) + (size_t)m * N
                      : static_cast<T*>(p.out) + (size_t)(ti.row0 + m) * N;
@@ -423,10 +460,17 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const St
   }(std::make_integer_sequence<int, C::UNROLL>{});
 }
 
-template <class C, bool kUp>
+// The combine tile of a shared-expert down tile reuses the token LDS buffers:
+// BM rows of BN bf16 outputs, rows padded by 16 bytes.
+template <int BM, int BN>
+constexpr int comb_ld() { return BN + 8; }
+
+template <class C, bool kUp, bool kComb = false>
 __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::LDS]) {
+  static_assert(!kComb || C::BM * comb_ld<C::BM, C::BN>() * 2 <= C::NB * C::LDS,
+                "the combine tile fits in the token buffers");
   TileInfo ti;
-  const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
+  const int32_t* sched = p.sched + (kUp ? 0 : kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, C::BM, ti)) return;
   const bool shared = ti.g == p.E;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -492,6 +536,29 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
   [&]<int... I>(std::integer_sequence<int, I...>) {
     ((m_active == I + 1 ? stream_kloop<C, I + 1>(sx, S, nk, acc) : void()), ...);
   }(std::make_integer_sequence<int, C::MT>{});
+  if constexpr (kComb) {
+    constexpr int LD = comb_ld<C::BM, C::BN>();
+    uint16_t* st = reinterpret_cast<uint16_t*>(&sx[0][0]);
+    __syncthreads();                  // every wave is done with the token buffers
+    if (wave_active) {
+      const int ml = lane & 31, rg = 4 * (lane >> 5);
+#pragma unroll
+      for (int a = 0; a < C::MT; ++a) {
+        const int r = 32 * a + ml;
+        if (a >= m_active || r >= rows_left) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 o;
+          o.x = (uint32_t)f32_to_bf16(acc[a][4 * q]) | ((uint32_t)f32_to_bf16(acc[a][4 * q + 1]) << 16);
+          o.y = (uint32_t)f32_to_bf16(acc[a][4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[a][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(st + r * LD + wave * 32 + 8 * q + rg) = o;
+        }
+      }
+    }
+    __syncthreads();
+    combine_from_lds<uint16_t>(p, st, LD, ti, ti.nt * C::BN, C::BN);
+    return;
+  }
   if (!wave_active) return;
 
   // epilogue: lane holds D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
@@ -668,14 +735,16 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
     for (int i = 0; i < 16; ++i) acc[a][i] *= sprev[a][i >> 3];
 }
 
-template <bool kUp, bool kNT>
+template <bool kUp, bool kNT, bool kComb = false>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_fp8_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[F8::NB][F8::LDS];
   __shared__ float2 sxs[F8::NB][F8::BM];
-  __shared__ float wamax[F8::WAVES][F8::BM];
+  __shared__ float wamax[kUp ? F8::WAVES : 1][F8::BM];
+  static_assert(!kComb || F8::BM * comb_ld<F8::BM, F8::BN>() * 2 <= F8::NB * F8::LDS,
+                "the combine tile fits in the token buffers");
   TileInfo ti;
-  const int32_t* sched = kUp ? p.sched : p.sched + p.E + 2;
+  const int32_t* sched = p.sched + (kUp ? 0 : kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, F8::BM, ti)) return;
   const bool shared = ti.g == p.E;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -777,6 +846,26 @@ void stream_fp8_kernel(FfnProblem p) {
       }
       if (wave == 0 && fg == 0) (shared ? p.hsscale : p.hscale)[row * (N / 128) + ti.nt] = scale;
     }
+  } else if constexpr (kComb) {
+    constexpr int LD = comb_ld<F8::BM, F8::BN>();
+    uint16_t* st = reinterpret_cast<uint16_t*>(&sx[0][0]);
+    __syncthreads();                  // every wave is done with the token buffers
+    if (wave_active) {
+#pragma unroll
+      for (int a = 0; a < kF8MT; ++a) {
+        const int r = 32 * a + ml;
+        if (a >= m_active || r >= rows_left) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 o;
+          o.x = (uint32_t)f32_to_bf16(acc[a][4 * q]) | ((uint32_t)f32_to_bf16(acc[a][4 * q + 1]) << 16);
+          o.y = (uint32_t)f32_to_bf16(acc[a][4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[a][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(st + r * LD + wave * 32 + 8 * q + rg) = o;
+        }
+      }
+    }
+    __syncthreads();
+    combine_from_lds<uint16_t>(p, st, LD, ti, ti.nt * F8::BN, F8::BN);
   } else {
     if (!wave_active) return;
 #pragma unroll
@@ -794,11 +883,11 @@ void stream_fp8_kernel(FfnProblem p) {
   }
 }
 
-template <class C, bool kUp>
+template <class C, bool kUp, bool kComb = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void stream_bf16_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[C::NB][C::LDS];
-  stream_tile<C, kUp>(p, sx);
+  stream_tile<C, kUp, kComb>(p, sx);
 }
 
 // ---------------------------------------------------------------------------
@@ -944,10 +1033,14 @@ __global__ __launch_bounds__(256) void up_skinny_fp8_kernel(FfnProblem p) {
   }
 }
 
-// Down projection, fp8, skinny tiles: 16 tokens x 256 output columns.
+// Down projection, fp8, skinny tiles: 16 tokens x 256 output columns
+// (kComb: the shared expert's tiles, ending with the fused combine).
+template <bool kComb>
 __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
+  constexpr int LD = kDnBN8 + 8;                    // LDS row of the combine tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[kComb ? 16 * LD : 1];
   TileInfo ti;
-  const int32_t* sched = p.sched + p.E + 2;
+  const int32_t* sched = p.sched + (kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, ti)) return;
   const bool shared = ti.g == p.E;
   const int K = shared ? p.inter_s : p.inter, KB = K / 128;
@@ -955,7 +1048,8 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int nbase = ti.nt * kDnBN8 + wave * 16 * kDnNT8;
-  if (nbase >= N) return;
+  if (!kComb && nbase >= N) return;
+  const bool active = nbase < N;                    // waves past the last column still meet the barrier
   const int mi = ti.m0 + min(r, ti.mrows - 1);
   const size_t hrow = shared ? (size_t)mi : (size_t)(ti.row0 + mi);
   const char* bp = reinterpret_cast<const char*>(static_cast<const uint8_t*>(shared ? p.hs : p.h) + hrow * K) + 32 * grp;
@@ -966,7 +1060,7 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   const float* sp[kDnNT8];
 #pragma unroll
   for (int j = 0; j < kDnNT8; ++j) {
-    const int n = nbase + 16 * j;
+    const int n = min(nbase + 16 * j, N - 16);
     ap[j] = reinterpret_cast<const char*>(W2) + wtile_off(n + r, 32 * grp, K);
     sp[j] = S2 + (size_t)(n / 128) * KB;
   }
@@ -993,14 +1087,28 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
       for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(part[i], sc, acc[j][i]);
     }
   };
-  load(0, 0);
-  for (int kb = 0; kb < KB; kb += 2) {
-    if (kb + 1 < KB) load(1, kb + 1);
-    comp(0, kb);
-    if (kb + 2 < KB) load(0, kb + 2);
-    if (kb + 1 < KB) comp(1, kb + 1);
+  if (active) {
+    load(0, 0);
+    for (int kb = 0; kb < KB; kb += 2) {
+      if (kb + 1 < KB) load(1, kb + 1);
+      comp(0, kb);
+      if (kb + 2 < KB) load(0, kb + 2);
+      if (kb + 1 < KB) comp(1, kb + 1);
+    }
   }
   const int m = ti.m0 + r;
+  if constexpr (kComb) {
+    if (active && r < ti.mrows) {
+#pragma unroll
+      for (int j = 0; j < kDnNT8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_tile[r * LD + wave * 16 * kDnNT8 + 16 * j + 4 * grp + i] = f32_to_bf16(acc[j][i]);
+    }
+    __syncthreads();
+    combine_from_lds<uint16_t>(p, s_tile, LD, ti, ti.nt * kDnBN8, kDnBN8);
+    return;
+  }
   if (r < ti.mrows) {
     uint16_t* orow = static_cast<uint16_t*>(shared ? p.shared_out : p.out) + (shared ? (size_t)m : (size_t)(ti.row0 + m)) * N;
 #pragma unroll
@@ -1047,17 +1155,20 @@ static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
   return Tiles::Skinny;
 }
 
-// Tile kind, tile sizes and grid sizes of the two projection launches.
+// Tile kind, tile sizes and grid sizes of the projection launches.
 struct FfnPlan {
   Tiles t;
   bool nt;              // stream tiles read their weights non-temporally
   int bm, nt_up, nt_up_s, nt_dn, threads;
-  long g_up, g_dn;      // workgroups (a multiple of 8)
+  long g_up, g_dn, g_dn_s;   // workgroups (multiples of 8): up, down, shared down + combine
 };
 
-static FfnPlan plan_ffn(const FfnProblem& p, bool has_shared) {
+static long round8(long n) { return (n + 7) / 8 * 8; }
+
+static FfnPlan plan_ffn(const FfnProblem& p) {
   FfnPlan L{};
   const long R = (long)p.ntok * p.topk;
+  const bool has_shared = p.inter_s > 0 && (p.shared_up || p.shared_down != SharedDown::None);
   L.t = pick_tiles(p, has_shared);
   const bool f8 = p.wkind == WKind::FP8;
   // stream tiles read their weights non-temporally while experts average
@@ -1074,15 +1185,18 @@ static FfnPlan plan_ffn(const FfnProblem& p, bool has_shared) {
   L.nt_up = ceil_div(p.inter, bn_up);
   L.nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
   L.nt_dn = ceil_div(p.dim, bn_dn);
-  L.g_up = (max_tiles(R, p.E, p.ntok, has_shared, L.bm, L.nt_up, L.nt_up_s) + 7) / 8 * 8;
-  L.g_dn = (max_tiles(R, p.E, p.ntok, has_shared, L.bm, L.nt_dn, L.nt_dn) + 7) / 8 * 8;
+  const long Rr = p.routed ? R : 0;
+  L.g_up = Rr || p.shared_up ? round8(max_tiles(Rr, p.E, p.ntok, p.shared_up, L.bm, L.nt_up, L.nt_up_s)) : 0;
+  const bool dn_store = p.shared_down == SharedDown::Store;
+  L.g_dn = Rr || dn_store ? round8(max_tiles(Rr, p.E, p.ntok, dn_store, L.bm, L.nt_dn, L.nt_dn)) : 0;
+  L.g_dn_s = p.shared_down == SharedDown::Combine ? round8((long)ceil_div(p.ntok, L.bm) * L.nt_dn) : 0;
   return L;
 }
 
 static long quant_blocks(int ntok, int dim) { return ((long)ntok * (dim / 128) * 16 + 255) / 256; }
 
 static long plan_items(const FfnProblem& p, const FfnPlan& L) {
-  long items = std::max(L.g_up, L.g_dn) * L.threads;
+  long items = std::max(std::max(L.g_up, L.g_dn), L.g_dn_s) * L.threads;
   if (p.wkind == WKind::FP8) items = std::max(items, quant_blocks(p.ntok, p.dim) * 256);
   return items;
 }
@@ -1092,32 +1206,54 @@ long ffn_max_items(int ntok, int topk, int E, int dim, int inter, int inter_s, W
   FfnProblem p{};
   p.ntok = ntok; p.topk = topk; p.E = E; p.dim = dim; p.inter = inter; p.inter_s = inter_s;
   p.wkind = wk;
-  return plan_items(p, plan_ffn(p, has_shared && inter_s > 0));
+  p.routed = true;
+  p.shared_up = has_shared && inter_s > 0;
+  // storing the shared output takes the largest down grid of the three ways
+  p.shared_down = p.shared_up ? SharedDown::Store : SharedDown::None;
+  return plan_items(p, plan_ffn(p));
+}
+
+// The down projection launch: routed (and stored shared) tiles, or with kComb
+// the shared expert's tiles fused with the combine.
+template <bool kComb>
+static void launch_down(const FfnProblem& q, const FfnPlan& L, int grid, hipStream_t st) {
+  const Tiles t = L.t;
+  const bool f8 = q.wkind == WKind::FP8, nt = L.nt;
+  if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<false, true, kComb><<<grid, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && f8) stream_fp8_kernel<false, false, kComb><<<grid, F8::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false, kComb><<<grid, SHuge::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false, kComb><<<grid, SBigNT::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<SBig, false, kComb><<<grid, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Mid) stream_bf16_kernel<SMid, false, kComb><<<grid, SMid::THREADS, 0, st>>>(q);
+  else if (f8) down_skinny_fp8_kernel<kComb><<<grid, 256, 0, st>>>(q);
+  else if (q.wkind == WKind::BF16) down_skinny_kernel<uint16_t, kComb><<<grid, 256, 0, st>>>(q);
+  else down_skinny_kernel<float, kComb><<<grid, 256, 0, st>>>(q);
 }
 
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
-  const bool has_shared = p.ws1 != nullptr && p.shared_out != nullptr && p.inter_s > 0;
-  const FfnPlan L = plan_ffn(p, has_shared);
+  const FfnPlan L = plan_ffn(p);
   // a launch counts its work-items in 32 bits; refuse before enqueuing anything
   if (plan_items(p, L) > kMaxLaunchItems) return hipErrorInvalidConfiguration;
   const Tiles t = L.t;
   const bool f8 = p.wkind == WKind::FP8, nt = L.nt;
-  ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.offsets, p.E, p.ntok, has_shared ? 1 : 0, L.bm, L.nt_up,
-                                          L.nt_up_s, L.bm, L.nt_dn, p.e_begin, p.e_end, p.sched);
+  ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.routed ? p.offsets : nullptr, p.E, p.ntok,
+                                          p.routed ? 1 : 0, p.shared_up ? 1 : 0,
+                                          (int)p.shared_down, L.bm, L.nt_up, L.nt_up_s, L.nt_dn,
+                                          p.e_begin, p.e_end, p.sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  FfnProblem q = p;
-  if (!has_shared) { q.ws1 = q.ws3 = q.ws2 = nullptr; q.shared_out = nullptr; }
-  const int g_up = (int)L.g_up, g_dn = (int)L.g_dn;
+  const FfnProblem& q = p;
+  const int g_up = (int)L.g_up, g_dn = (int)L.g_dn, g_dn_s = (int)L.g_dn_s;
   auto mark = [&](int i) { if (p.ev[i]) (void)hipEventRecord(p.ev[i], st); };
-  if (f8) {   // quantise x once (the 1x128 blocks do not depend on the expert)
+  if (f8 && g_up) {   // quantise x once (the 1x128 blocks do not depend on the expert)
     quant_fp8_kernel<<<(int)quant_blocks(p.ntok, p.dim), 256, 0, st>>>(
         static_cast<const uint16_t*>(p.x), p.ntok, p.dim, const_cast<uint8_t*>(p.xq),
         const_cast<float*>(p.xs));
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   mark(0);
-  if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<true, true><<<g_up, F8::THREADS, 0, st>>>(q);
+  if (g_up == 0) {}
+  else if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<true, true><<<g_up, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big && f8) stream_fp8_kernel<true, false><<<g_up, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, true><<<g_up, SHuge::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, true><<<g_up, SBigNT::THREADS, 0, st>>>(q);
@@ -1129,15 +1265,9 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   mark(1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   mark(2);
-  if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<false, true><<<g_dn, F8::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big && f8) stream_fp8_kernel<false, false><<<g_dn, F8::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false><<<g_dn, SHuge::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false><<<g_dn, SBigNT::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big) stream_bf16_kernel<SBig, false><<<g_dn, SBig::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Mid) stream_bf16_kernel<SMid, false><<<g_dn, SMid::THREADS, 0, st>>>(q);
-  else if (p.wkind == WKind::FP8) down_skinny_fp8_kernel<<<g_dn, 256, 0, st>>>(q);
-  else if (p.wkind == WKind::BF16) down_skinny_kernel<uint16_t><<<g_dn, 256, 0, st>>>(q);
-  else down_skinny_kernel<float><<<g_dn, 256, 0, st>>>(q);
+  if (g_dn) launch_down<false>(q, L, g_dn, st);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (g_dn_s) launch_down<true>(q, L, g_dn_s, st);
   mark(3);
   return hipGetLastError();
 }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "combine.h"
+
 namespace moe {
 
 constexpr int kMaxExperts = 512;
@@ -29,6 +31,9 @@ hipError_t launch_permute(const int32_t* idx, int ntok, int topk, int E, int32_t
 // ffn.hip
 enum class WKind { F32, BF16, FP8 };
 
+// What the shared expert's down projection does with its output.
+enum class SharedDown { None, Store, Combine };
+
 struct FfnProblem {
   const void* x;               // [T, dim] act dtype (bf16 or f32)
   const uint8_t* xq;           // fp8 path: [T, dim] e4m3 codes of x
@@ -44,14 +49,21 @@ struct FfnProblem {
   void* hs;                    // shared h [T, inter_s]
   float* hsscale;              // fp8: shared h scales [T, inter_s/128]
   void* out;                   // routed outputs [T*topk, dim] act dtype
-  void* shared_out;            // shared outputs [T, dim] act dtype (NULL = skip)
-  int32_t* sched;              // scratch, 2 * (E + 2) ints
+  void* shared_out;            // shared outputs [T, dim] act dtype (SharedDown::Store)
+  int32_t* sched;              // scratch, 3 * (E + 2) ints
   int ntok, dim, E, topk, inter, inter_s;
   int e_begin, e_end;          // routed experts computed: [e_begin, e_end)
   bool act_f32;
   WKind wkind;
+  bool routed;                 // compute the routed experts (offsets, sorted_token, out)
+  bool shared_up;              // the shared expert's up projection (needs ws1, ws3, hs)
+  SharedDown shared_down;      // its down projection: skipped, stored, or fused with the combine
+  CombineArgs comb;            // SharedDown::Combine: the routed rows, weights and y
   hipEvent_t ev[4];            // optional timing: up start/end, down start/end (or null)
 };
+
+// The fused combine needs the token's slots sorted in registers.
+inline bool ffn_can_fuse_combine(int topk) { return topk <= kRegSlots; }
 
 size_t ffn_h_bytes(int ntok, int topk, int inter, int inter_s, WKind wk, bool act_f32);
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t st);
@@ -60,6 +72,7 @@ constexpr long kMaxLaunchItems = 0xFFFFFFFFL;
 // Work-items of the largest launch launch_ffn makes for these shapes (host only).
 long ffn_max_items(int ntok, int topk, int E, int dim, int inter, int inter_s, WKind wk,
                    bool has_shared);
+constexpr int kSchedInts(int E) { return 3 * (E + 2); }
 hipError_t launch_quant_x(const uint16_t* x, int ntok, int dim, uint8_t* xq, float* xs,
                           hipStream_t st);
 
@@ -70,14 +83,9 @@ hipError_t launch_pack_weights(const uint8_t* src, int64_t rows, int64_t row_byt
 // calib.hip (measurement only): one streaming read of bytes (multiple of 16)
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 
-// combine.hip
-// layer_acc: accumulate in the layer dtype over the experts in ascending id
-// (rows ascend with the expert id), casting after every addition.
-// offsets (may be NULL for all experts): only rows [offsets[e_begin],
-// offsets[e_end]) - the experts of the range - are added.
-hipError_t launch_combine(const void* expert_out, const int32_t* row_of, const float* topk_w,
-                          const void* shared_out, void* y, int ntok, int dim, int topk,
-                          bool act_f32, bool layer_acc, const int32_t* offsets, int e_begin,
-                          int e_end, hipStream_t st);
+// combine.hip: the stand-alone combine, y = cast(sum_k w O + S) with the
+// arithmetic of combine.h; shared_out may be NULL (no shared expert).
+hipError_t launch_combine(const CombineArgs& c, const void* shared_out, int ntok, int dim,
+                          bool act_f32, hipStream_t st);
 
 }  // namespace moe

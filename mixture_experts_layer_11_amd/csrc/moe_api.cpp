@@ -82,7 +82,7 @@ Layout layout(const moe_params* p, int64_t T) {
   L.sorted_token = take(R * 4);
   L.row_of = take(R * 4);
   L.perm = take(moe::permute_scratch_bytes((int)T, (int)E));
-  L.sched = take(2 * (E + 2) * 4);
+  L.sched = take((size_t)moe::kSchedInts((int)E) * 4);
   L.h = take(R * p->inter * hsz);
   L.hscale = take(fp8 ? R * (p->inter / 128) * 4 : 0);
   L.hs = take((size_t)T * p->shared_inter * hsz);
@@ -178,17 +178,16 @@ moe_status do_permute(const moe_params* p, int64_t T, const int32_t* idx, int32_
   return e == hipSuccess ? MOE_OK : hip_fail(e, "permute launch");
 }
 
-moe_status do_ffn(const moe_params* p, int64_t T, const void* x, const int32_t* sorted_token,
-                  const int32_t* offsets, const moe_weights* w, void* out, void* shared_out,
-                  void* ws, hipStream_t st) {
+// The parts of an expert-step problem every call shares: shapes, weights,
+// workspace buffers.  The caller sets what runs (routed / shared / combine).
+moe::FfnProblem ffn_problem(const moe_params* p, int64_t T, const void* x, const moe_weights* w,
+                            void* ws) {
   const Layout L = layout(p, T);
   moe::FfnProblem f{};
   f.x = x;
-  f.sorted_token = sorted_token;
-  f.offsets = offsets;
   f.w1 = w->w1; f.w3 = w->w3; f.w2 = w->w2;
   f.w1s = w->w1_scale; f.w3s = w->w3_scale; f.w2s = w->w2_scale;
-  if (shared_out != nullptr && p->shared_inter > 0) {
+  if (p->shared_inter > 0) {
     f.ws1 = w->ws1; f.ws3 = w->ws3; f.ws2 = w->ws2;
     f.ws1s = w->ws1_scale; f.ws3s = w->ws3_scale; f.ws2s = w->ws2_scale;
   }
@@ -198,26 +197,68 @@ moe_status do_ffn(const moe_params* p, int64_t T, const void* x, const int32_t* 
   f.hsscale = at<float>(ws, L.hsscale);
   f.xq = at<uint8_t>(ws, L.xq);
   f.xs = at<float>(ws, L.xs);
-  f.out = out;
-  f.shared_out = f.ws1 != nullptr ? shared_out : nullptr;
   f.sched = at<int32_t>(ws, L.sched);
   f.ntok = (int)T; f.dim = p->dim; f.E = p->n_experts; f.topk = p->topk;
   f.inter = p->inter; f.inter_s = p->shared_inter;
   f.e_begin = p->expert_begin; f.e_end = expert_end(p);
   f.act_f32 = p->act_dtype == MOE_F32;
   f.wkind = wkind(p);
+  f.shared_down = moe::SharedDown::None;
+  return f;
+}
+
+moe_status run_ffn(moe::FfnProblem& f, hipStream_t st) {
   profile_slot(f.ev);
   hipError_t e = moe::launch_ffn(f, st);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "expert launch");
 }
 
-moe_status check_weights(const moe_params* p, const moe_weights* w, bool need_router, bool need_shared) {
+// The shared expert and the combine (moe_combine, and the end of moe_forward,
+// where f already holds the routed work).  With a shared expert and at most
+// kRegSlots experts per token the combine is fused into the shared expert's
+// down projection; otherwise the shared output goes through the workspace
+// and the stand-alone combine adds it.
+moe_status shared_and_combine(const moe_params* p, int64_t T, moe::FfnProblem& f,
+                              const moe::CombineArgs& c, void* ws, hipStream_t st) {
+  const Layout L = layout(p, T);
+  const bool shared = p->shared_inter > 0;
+  const bool fuse = shared && moe::ffn_can_fuse_combine(p->topk);
+  f.shared_up = shared;
+  f.shared_down = fuse ? moe::SharedDown::Combine : shared ? moe::SharedDown::Store : moe::SharedDown::None;
+  f.comb = c;
+  f.shared_out = shared ? at<void>(ws, L.shared_out) : nullptr;
+  moe_status s = MOE_OK;
+  if (f.routed || shared) s = run_ffn(f, st);
+  if (s != MOE_OK || fuse) return s;
+  hipError_t e = moe::launch_combine(c, f.shared_out, (int)T, p->dim, p->act_dtype == MOE_F32, st);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+}
+
+moe::CombineArgs combine_args(const moe_params* p, const void* expert_out, const int32_t* row_of,
+                              const float* topk_w, void* y, const int32_t* offsets) {
+  moe::CombineArgs c{};
+  c.out = expert_out;
+  c.row_of = row_of;
+  c.w = topk_w;
+  c.y = y;
+  c.offsets = full_range(p) ? nullptr : offsets;
+  c.e_begin = p->expert_begin;
+  c.e_end = expert_end(p);
+  c.topk = p->topk;
+  c.layer_acc = p->accumulate == MOE_ACC_LAYER;
+  return c;
+}
+
+moe_status check_weights(const moe_params* p, const moe_weights* w, bool need_router,
+                         bool need_shared, bool need_routed = true) {
   if (w == nullptr) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (need_router && w->w_router == nullptr) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
-  if (!w->w1 || !w->w3 || !w->w2) return fail(MOE_ERR_INVALID_ARG, "w1/w3/w2 must be non-NULL");
   const bool fp8 = p->weight_dtype == MOE_FP8_E4M3;
-  if (fp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale))
-    return fail(MOE_ERR_INVALID_ARG, "fp8 weights need w1/w3/w2 scales");
+  if (need_routed) {
+    if (!w->w1 || !w->w3 || !w->w2) return fail(MOE_ERR_INVALID_ARG, "w1/w3/w2 must be non-NULL");
+    if (fp8 && (!w->w1_scale || !w->w3_scale || !w->w2_scale))
+      return fail(MOE_ERR_INVALID_ARG, "fp8 weights need w1/w3/w2 scales");
+  }
   if (need_shared && p->shared_inter > 0) {
     if (!w->ws1 || !w->ws3 || !w->ws2) return fail(MOE_ERR_INVALID_ARG, "shared_inter > 0 needs ws1/ws3/ws2");
     if (fp8 && (!w->ws1_scale || !w->ws3_scale || !w->ws2_scale))
@@ -328,36 +369,44 @@ moe_status moe_permute(const moe_params* p, int64_t T, const int32_t* topk_idx, 
 
 moe_status moe_expert_ffn(const moe_params* p, int64_t T, const void* x,
                           const int32_t* sorted_token, const int32_t* offsets,
-                          const moe_weights* w, void* expert_out, void* shared_out,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          const moe_weights* w, void* expert_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   g_err.clear();
   moe_status s = validate(p, T);
   if (s != MOE_OK) return s;
-  if (shared_out != nullptr && p->shared_inter == 0)
-    return fail(MOE_ERR_INVALID_ARG, "shared_out must be NULL when shared_inter = 0");
-  if ((s = check_launch_size(p, T, shared_out != nullptr)) != MOE_OK) return s;
-  if ((s = check_weights(p, w, false, shared_out != nullptr)) != MOE_OK) return s;
+  if ((s = check_launch_size(p, T, false)) != MOE_OK) return s;
+  if ((s = check_weights(p, w, false, false)) != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!x || !sorted_token || !offsets || !expert_out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
   if ((s = check_ws(p, T, workspace, workspace_bytes)) != MOE_OK) return s;
-  return do_ffn(p, T, x, sorted_token, offsets, w, expert_out, shared_out, workspace,
-                (hipStream_t)stream);
+  moe::FfnProblem f = ffn_problem(p, T, x, w, workspace);
+  f.routed = true;
+  f.sorted_token = sorted_token;
+  f.offsets = offsets;
+  f.out = expert_out;
+  return run_ffn(f, (hipStream_t)stream);
 }
 
-moe_status moe_combine(const moe_params* p, int64_t T, const void* expert_out,
-                       const int32_t* row_of, const float* topk_w, const void* shared_out,
-                       void* y, void* stream) {
+moe_status moe_combine(const moe_params* p, int64_t T, const void* x, const void* expert_out,
+                       const int32_t* row_of, const float* topk_w, const moe_weights* w, void* y,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   moe_status s = validate(p, T);
   if (s != MOE_OK) return s;
+  if (!full_range(p)) return fail(MOE_ERR_UNSUPPORTED, "moe_combine needs the full expert range");
+  const bool shared = p->shared_inter > 0;
+  if (shared) {
+    if ((s = check_weights(p, w, false, true, false)) != MOE_OK) return s;
+    if ((s = check_launch_size(p, T, true)) != MOE_OK) return s;
+  }
   if (T == 0) return MOE_OK;
   if (!expert_out || !row_of || !topk_w || !y) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
-  if (!full_range(p)) return fail(MOE_ERR_UNSUPPORTED, "moe_combine needs the full expert range");
-  hipError_t e = moe::launch_combine(expert_out, row_of, topk_w, shared_out, y, (int)T, p->dim,
-                                     p->topk, p->act_dtype == MOE_F32,
-                                     p->accumulate == MOE_ACC_LAYER, nullptr, 0, p->n_experts,
-                                     (hipStream_t)stream);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+  if (shared && !x) return fail(MOE_ERR_INVALID_ARG, "x is NULL (needed by the shared expert)");
+  if ((s = check_ws(p, T, workspace, workspace_bytes)) != MOE_OK) return s;
+  const moe::CombineArgs c = combine_args(p, expert_out, row_of, topk_w, y, nullptr);
+  moe::FfnProblem f = shared ? ffn_problem(p, T, x, w, workspace) : moe::FfnProblem{};
+  f.routed = false;
+  return shared_and_combine(p, T, f, c, workspace, (hipStream_t)stream);
 }
 
 moe_status moe_quant_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* q, float* scales,
@@ -417,14 +466,14 @@ moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_
   int32_t* st_tok = at<int32_t>(workspace, L.sorted_token);
   int32_t* row_of = at<int32_t>(workspace, L.row_of);
   void* out = at<void>(workspace, L.out);
-  void* sh = p->shared_inter > 0 ? at<void>(workspace, L.shared_out) : nullptr;
   if ((s = do_gate(p, T, x, w->w_router, w->bias, idx, wt, workspace, st)) != MOE_OK) return s;
   if ((s = do_permute(p, T, idx, cnt, off, st_tok, row_of, workspace, st)) != MOE_OK) return s;
-  if ((s = do_ffn(p, T, x, st_tok, off, w, out, sh, workspace, st)) != MOE_OK) return s;
-  hipError_t e = moe::launch_combine(out, row_of, wt, sh, y, (int)T, p->dim, p->topk,
-                                     p->act_dtype == MOE_F32, p->accumulate == MOE_ACC_LAYER,
-                                     full_range(p) ? nullptr : off, p->expert_begin, expert_end(p), st);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "combine launch");
+  moe::FfnProblem f = ffn_problem(p, T, x, w, workspace);
+  f.routed = true;
+  f.sorted_token = st_tok;
+  f.offsets = off;
+  f.out = out;
+  return shared_and_combine(p, T, f, combine_args(p, out, row_of, wt, y, off), workspace, st);
 }
 
 }  // extern "C"

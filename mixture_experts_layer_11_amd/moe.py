@@ -70,8 +70,8 @@ def lib() -> ctypes.CDLL:
         "moe_workspace_size": (st, [P, i64, ctypes.POINTER(sz)]),
         "moe_gate": (st, [P, i64, _VP, _VP, _VP, _VP, _VP, _VP, sz, _VP]),
         "moe_permute": (st, [P, i64, _VP, _VP, _VP, _VP, _VP, _VP, sz, _VP]),
-        "moe_expert_ffn": (st, [P, i64, _VP, _VP, _VP, W, _VP, _VP, _VP, sz, _VP]),
-        "moe_combine": (st, [P, i64, _VP, _VP, _VP, _VP, _VP, _VP]),
+        "moe_expert_ffn": (st, [P, i64, _VP, _VP, _VP, W, _VP, _VP, sz, _VP]),
+        "moe_combine": (st, [P, i64, _VP, _VP, _VP, _VP, W, _VP, _VP, sz, _VP]),
         "moe_forward": (st, [P, i64, _VP, W, _VP, _VP, _VP, _VP, _VP, sz, _VP]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -210,24 +210,29 @@ class DeviceWeights:
         return moe_weights(*[_ptr(getattr(self, f)) for f, _ in moe_weights._fields_])
 
 
-def moe_expert_ffn(p: Params, x, sorted_token, offsets, w: DeviceWeights, workspace,
-                   with_shared=True, stream=None):
+def moe_expert_ffn(p: Params, x, sorted_token, offsets, w: DeviceWeights, workspace, out=None,
+                   stream=None):
+    """Routed experts -> expert_out [T*topk, dim] in the expert-contiguous order."""
     T = x.shape[0]
-    out = torch.empty((T * p.topk, p.dim), dtype=p.act_torch, device=x.device)
-    sh = (torch.empty((T, p.dim), dtype=p.act_torch, device=x.device)
-          if with_shared and p.shared_inter > 0 else None)
+    out = out if out is not None else torch.empty((T * p.topk, p.dim), dtype=p.act_torch,
+                                                  device=x.device)
     cw = w.c()
     _check(lib().moe_expert_ffn(ctypes.byref(p.c()), T, _ptr(x), _ptr(sorted_token),
-                                _ptr(offsets), ctypes.byref(cw), _ptr(out), _ptr(sh),
+                                _ptr(offsets), ctypes.byref(cw), _ptr(out),
                                 _ptr(workspace), workspace.numel(), _stream(stream)))
-    return out, sh
+    return out
 
 
-def moe_combine(p: Params, expert_out, row_of, topk_w, shared_out, y=None, stream=None):
+def moe_combine(p: Params, x, expert_out, row_of, topk_w, w: Optional[DeviceWeights], workspace,
+                y=None, stream=None):
+    """Shared expert on x plus the weighted combine of the routed outputs -> y [T, dim].
+    w supplies the shared weights (may be None when p.shared_inter == 0)."""
     T = row_of.shape[0]
     y = y if y is not None else torch.empty((T, p.dim), dtype=p.act_torch, device=row_of.device)
-    _check(lib().moe_combine(ctypes.byref(p.c()), T, _ptr(expert_out), _ptr(row_of),
-                             _ptr(topk_w), _ptr(shared_out), _ptr(y), _stream(stream)))
+    cw = None if w is None else w.c()
+    _check(lib().moe_combine(ctypes.byref(p.c()), T, _ptr(x), _ptr(expert_out), _ptr(row_of),
+                             _ptr(topk_w), None if cw is None else ctypes.byref(cw), _ptr(y),
+                             _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
 
 

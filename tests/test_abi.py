@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(L, name), name
     assert set(moe.EXPORTS) == set(declared_functions())
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -96,7 +96,10 @@ def test_oversized_expert_launch_rejected_before_enqueue():
     T = (1 << 24) - 1
     assert _ws_status(p, T)[0] == moe.MOE_OK          # the shapes themselves are valid
     s = L.moe_expert_ffn(ctypes.byref(p.c()), T, fake, fake, fake, ctypes.byref(w), fake,
-                         fake, fake, 1 << 62, None)
+                         fake, 1 << 62, None)
+    assert s == moe.MOE_ERR_UNSUPPORTED and "work-items" in L.moe_last_error().decode()
+    s = L.moe_combine(ctypes.byref(p.c()), T, fake, fake, fake, fake, ctypes.byref(w), fake,
+                      fake, 1 << 62, None)
     assert s == moe.MOE_ERR_UNSUPPORTED and "work-items" in L.moe_last_error().decode()
     s = L.moe_forward(ctypes.byref(p.c()), T, fake, ctypes.byref(w), fake, None, None, None,
                       fake, 1 << 62, None)
@@ -104,7 +107,7 @@ def test_oversized_expert_launch_rejected_before_enqueue():
     # a decode-sized batch of the same layer passes the check and stops at the
     # (deliberately too small) workspace instead
     s = L.moe_expert_ffn(ctypes.byref(p.c()), 16, fake, fake, fake, ctypes.byref(w), fake,
-                         fake, fake, 16, None)
+                         fake, 16, None)
     assert s == moe.MOE_ERR_WORKSPACE
 
 
@@ -140,7 +143,9 @@ def test_combine_needs_full_expert_range():
     pc = _p().c()
     pc.expert_begin, pc.expert_end = 0, 32
     fake = ctypes.c_void_p(256)
-    s = moe.lib().moe_combine(ctypes.byref(pc), 16, fake, fake, fake, None, fake, None)
+    w = moe.moe_weights(ws1=256, ws3=256, ws2=256)
+    s = moe.lib().moe_combine(ctypes.byref(pc), 16, fake, fake, fake, fake, ctypes.byref(w), fake,
+                              fake, 1 << 30, None)
     assert s == moe.MOE_ERR_UNSUPPORTED
 
 
@@ -171,12 +176,20 @@ def test_null_and_workspace_errors_enqueue_nothing():
     p1 = _p(n_experts=8, n_groups=8, topk_groups=4, topk=4)
     s = L.moe_gate(ctypes.byref(p1.c()), i64, fake, fake, fake, fake, fake, None, 0, None)
     assert s == moe.MOE_ERR_INVALID_ARG
-    # shared_out given without a shared expert
-    p0 = _p(shared_inter=0)
+    # a shared expert without its weights, and a combine without x for it
     w = moe.moe_weights(w1=256, w3=256, w2=256)
-    s = L.moe_expert_ffn(ctypes.byref(p0.c()), i64, fake, fake, fake, ctypes.byref(w), fake,
-                         fake, fake, 1 << 30, None)
-    assert s == moe.MOE_ERR_INVALID_ARG
+    s = L.moe_combine(ctypes.byref(pc), i64, fake, fake, fake, fake, ctypes.byref(w), fake,
+                      fake, 1 << 30, None)
+    assert s == moe.MOE_ERR_INVALID_ARG and "ws1" in L.moe_last_error().decode()
+    ws = moe.moe_weights(ws1=256, ws3=256, ws2=256)
+    s = L.moe_combine(ctypes.byref(pc), i64, None, fake, fake, fake, ctypes.byref(ws), fake,
+                      fake, 1 << 30, None)
+    assert s == moe.MOE_ERR_INVALID_ARG and "x is NULL" in L.moe_last_error().decode()
+    # without a shared expert the combine needs neither x nor weights
+    p0 = _p(shared_inter=0)
+    s = L.moe_combine(ctypes.byref(p0.c()), i64, None, fake, fake, fake, None, fake,
+                      None, 0, None)
+    assert s == moe.MOE_ERR_WORKSPACE
     # fp8 weights without scales
     p8 = _p(weight_dtype="fp8")
     s = L.moe_forward(ctypes.byref(p8.c()), i64, fake, ctypes.byref(w), fake, None, None, None,

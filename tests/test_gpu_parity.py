@@ -50,6 +50,17 @@ def _x_dev(layer):
     return moe.to_device(layer.x, layer.cfg.act_dtype)
 
 
+def shared_only(p, x, dw, ws):
+    """The shared expert's output alone, through moe_combine with every routing
+    weight 0 and zero expert outputs: each routed term is 0 * 0 = 0 and
+    0 + S = S exactly, so y = S (the shared module's output in the layer dtype)."""
+    T = x.shape[0]
+    row_of = torch.arange(T * p.topk, dtype=torch.int32, device=DEV).reshape(T, p.topk)
+    w = torch.zeros((T, p.topk), dtype=torch.float32, device=DEV)
+    eo = torch.zeros((T * p.topk, p.dim), dtype=p.act_torch, device=DEV)
+    return moe.moe_combine(p, x, eo, row_of, w, dw, ws)
+
+
 # ---------------------------------------------------------------------------
 # gate
 # ---------------------------------------------------------------------------
@@ -198,8 +209,9 @@ def test_expert_ffn_parity(cfg, layers):
     counts, offsets, sorted_token, row_of = oracle.permute(idx, cfg.E)
     p = moe.Params.from_config(cfg)
     ws = moe.alloc_workspace(p, cfg.T)
-    out, sh = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
-                                 torch.from_numpy(offsets).to(DEV), dw, ws)
+    out = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
+                             torch.from_numpy(offsets).to(DEV), dw, ws)
+    sh = shared_only(p, _x_dev(layer), dw, ws) if cfg.inter_shared else None
     _sync()
     out = moe.to_host_values(out)
     xv = oracle.moe_oracle.decode_act(layer.x, cfg.act_dtype)
@@ -261,8 +273,8 @@ def test_expert_ffn_tile_boundaries(name, kw, counts):
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     p = moe.Params.from_config(cfg)
     ws = moe.alloc_workspace(p, T)
-    out, _ = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
-                                torch.from_numpy(offsets).to(DEV), dw, ws)
+    out = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
+                             torch.from_numpy(offsets).to(DEV), dw, ws)
     _sync()
     out = moe.to_host_values(out)
     xv = oracle.moe_oracle.decode_act(layer.x, cfg.act_dtype)
@@ -314,8 +326,9 @@ def test_fp8_fused_h_quantisation(name, kw):
     counts, offsets, sorted_token, row_of = oracle.permute(idx, cfg.E)
     p = moe.Params.from_config(cfg)
     ws = moe.alloc_workspace(p, cfg.T)
-    out, sh = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
-                                 torch.from_numpy(offsets).to(DEV), dw, ws)
+    out = moe.moe_expert_ffn(p, _x_dev(layer), torch.from_numpy(sorted_token).to(DEV),
+                             torch.from_numpy(offsets).to(DEV), dw, ws)
+    sh = shared_only(p, _x_dev(layer), dw, ws)
     _sync()
     xv = oracle.moe_oracle.decode_act(layer.x, cfg.act_dtype)
     no_hq = _fp8_ffn_with("h_unquantised")
@@ -342,14 +355,18 @@ def test_fp8_fused_h_quantisation(name, kw):
     mut[R:] = no_hq(*sargs)
     d = np.abs(got - ref)
     off = d > _bf16_ulp(ref)                       # beyond one bf16 step
-    # one e4m3 step at the value's magnitude: 1/8 of it for normal codes, and
-    # the fixed subnormal spacing 2^-9 x the block scale (block max / 448) below
+    # one e4m3 step at the value's magnitude (1/8 of it for normal codes) plus
+    # one subnormal code (2^-9 x the block scale, block max / 448): an h within
+    # a few fp32 ulps of zero can round to +1 code on one side and -1 on the other
     bmax = np.abs(ref).reshape(ref.shape[0], -1, 128).max(axis=2).repeat(128, axis=1)
-    step = np.maximum(np.abs(ref) / 8, bmax / 448 * 2.0 ** -9)
-    far = d > step * (1 + 2.0 ** -7) + _bf16_ulp(ref)
+    sub = bmax / 448 * 2.0 ** -9
+    step = np.maximum(np.abs(ref) / 8, sub)
+    far = d > (step + sub) * (1 + 2.0 ** -7) + _bf16_ulp(ref)
     off_mut = np.abs(got - mut) > _bf16_ulp(mut)
+    worst = np.argsort((d / (step + sub)).ravel())[-3:]
     record("fp8_fused_h", case=name, elements=int(got.size), off_by_more_than_bf16_ulp=float(off.mean()),
-           beyond_one_e4m3_step=int(far.sum()), vs_unquantised_h=float(off_mut.mean()))
+           beyond_one_e4m3_step=int(far.sum()), vs_unquantised_h=float(off_mut.mean()),
+           worst=[[float(got.ravel()[i]), float(ref.ravel()[i]), float(sub.ravel()[i])] for i in worst])
     assert not far.any()
     assert off.mean() <= 5e-3
     assert off_mut.mean() >= 0.3
@@ -402,60 +419,80 @@ def test_pack_weights_bitexact(rows, row_bytes):
 # ---------------------------------------------------------------------------
 # combine (synthetic expert outputs, oracle dispatch)
 # ---------------------------------------------------------------------------
+# The shared expert used here has an output both sides compute exactly:
+# x[:, 0] = 1 and W1 = 32 on that column gives a1 = 32 for every h column,
+# silu(32) = 32 (1 - 1.3e-14) rounds to 32 in fp32 and bf16; W3 picks
+# x[:, 1 + j] for h column j, so h_j = 32 x[:, 1 + j] exactly; W2 picks
+# h_(n mod I) for output column n.  S is therefore 32 x[:, 1 + n mod I] in
+# the layer dtype, the combine's arithmetic is the only thing left to
+# compare, and it must be bit-exact: same fp32 operations in the same order
+# (ascending expert id, product then sum, shared output last).
 
-@pytest.mark.parametrize("act", ["bf16", "f32"])
-@pytest.mark.parametrize("K", [6, 12])          # the 8-slot and the 32-slot kernels
-def test_combine_parity(act, K):
-    rng = np.random.default_rng(5 + K)
-    T, E, dim = 203, 40, 320
-    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
-    w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
-    counts, offsets, sorted_token, row_of = oracle.permute(idx, E)
-    vals = rng.standard_normal((T * K, dim)).astype(np.float32)
-    shv = rng.standard_normal((T, dim)).astype(np.float32)
-    if act == "bf16":
-        vals_s, sh_s = inputs.f32_to_bf16_bits(vals), inputs.f32_to_bf16_bits(shv)
-        vals, shv = inputs.bf16_bits_to_f32(vals_s), inputs.bf16_bits_to_f32(sh_s)
-    else:
-        vals_s, sh_s = vals, shv
-    p = moe.Params(dim=dim, n_experts=E, n_groups=1, topk_groups=1, topk=K, inter=64,
-                   shared_inter=64, score_func="sigmoid", route_scale=1.0, act_dtype=act,
-                   router_dtype=act, weight_dtype=act)
-    y = moe.moe_combine(p, moe.to_device(vals_s, act), torch.from_numpy(row_of).to(DEV),
-                        torch.from_numpy(w).to(DEV), moe.to_device(sh_s, act))
-    _sync()
-    outs = vals[row_of]                                      # [T, K, dim]
-    ref = oracle.moe_oracle.round_to(oracle.combine(outs, w, idx, shv).astype(np.float64), act)
-    # the same fp32 operations in the same order (ascending expert id, product
-    # then sum, shared last), so the result is bit-exact
-    np.testing.assert_array_equal(moe.to_host_values(y).astype(np.float64), ref)
+def _exact_shared(act, dim, inter_s):
+    w1 = np.zeros((inter_s, dim), np.float32)
+    w1[:, 0] = 32.0
+    w3 = np.zeros((inter_s, dim), np.float32)
+    w3[np.arange(inter_s), 1 + np.arange(inter_s)] = 1.0
+    w2 = np.zeros((dim, inter_s), np.float32)
+    w2[np.arange(dim), np.arange(dim) % inter_s] = 1.0
+    enc = (lambda a: inputs.f32_to_bf16_bits(a)) if act == "bf16" else (lambda a: a)
+    mat = lambda a: moe.moe_pack_weights(moe.to_device(enc(a), act))
+    dw = moe.DeviceWeights(None, None, None, None, None, ws1=mat(w1), ws3=mat(w3), ws2=mat(w2))
+    return dw, (enc(w1), enc(w3), enc(w2))
 
 
-@pytest.mark.parametrize("act", ["bf16", "f32"])
-@pytest.mark.parametrize("K", [8, 20])
-def test_combine_layer_accumulator_bitexact(act, K):
-    # same arithmetic in the same order (ascending expert id, a cast after every
-    # addition), so the result is bit-exact
-    rng = np.random.default_rng(6 + K)
-    T, E, dim = 157, 48, 256
+def _combine_case(act, K, shared, seed, accumulate):
+    rng = np.random.default_rng(seed)
+    T, E, dim, inter_s = 203, 40, 320, (128 if shared else 0)
     idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
     w = rng.uniform(0.05, 1.0, (T, K)).astype(np.float32)
     counts, offsets, sorted_token, row_of = oracle.permute(idx, E)
     vals = (rng.standard_normal((T * K, dim)) * 2.0).astype(np.float32)
-    shv = rng.standard_normal((T, dim)).astype(np.float32)
+    x = rng.standard_normal((T, dim)).astype(np.float32)
+    x[:, 0] = 1.0
     if act == "bf16":
-        vals_s, sh_s = inputs.f32_to_bf16_bits(vals), inputs.f32_to_bf16_bits(shv)
-        vals, shv = inputs.bf16_bits_to_f32(vals_s), inputs.bf16_bits_to_f32(sh_s)
+        vals_s, x_s = inputs.f32_to_bf16_bits(vals), inputs.f32_to_bf16_bits(x)
+        vals, x = inputs.bf16_bits_to_f32(vals_s), inputs.bf16_bits_to_f32(x_s)
     else:
-        vals_s, sh_s = vals, shv
+        vals_s, x_s = vals, x
     p = moe.Params(dim=dim, n_experts=E, n_groups=1, topk_groups=1, topk=K, inter=64,
-                   shared_inter=64, score_func="sigmoid", route_scale=1.0, act_dtype=act,
-                   router_dtype=act, weight_dtype=act, accumulate="layer")
-    y = moe.moe_combine(p, moe.to_device(vals_s, act), torch.from_numpy(row_of).to(DEV),
-                        torch.from_numpy(w).to(DEV), moe.to_device(sh_s, act))
+                   shared_inter=inter_s, score_func="sigmoid", route_scale=1.0, act_dtype=act,
+                   router_dtype=act, weight_dtype=act, accumulate=accumulate)
+    dw, host_w = _exact_shared(act, dim, inter_s) if shared else (None, None)
+    ws = moe.alloc_workspace(p, T)
+    y = moe.moe_combine(p, moe.to_device(x_s, act), moe.to_device(vals_s, act),
+                        torch.from_numpy(row_of).to(DEV), torch.from_numpy(w).to(DEV), dw, ws)
     _sync()
-    ref = oracle.combine_layer(vals[row_of], w, idx, shv, act)
+    S = None
+    if shared:
+        S = 32.0 * x[:, 1 + np.arange(dim) % inter_s].astype(np.float64)
+        # the oracle's own shared expert gives exactly this closed form
+        so = oracle.expert_ffn(x.astype(np.float64), *host_w, act, act)
+        np.testing.assert_array_equal(so, S)
+    outs = vals[row_of]                                      # [T, K, dim]
+    if accumulate == "layer":
+        ref = oracle.combine_layer(outs, w, idx, S, act)
+    else:
+        ref = oracle.moe_oracle.round_to(oracle.combine(outs, w, idx, S).astype(np.float64), act)
     np.testing.assert_array_equal(moe.to_host_values(y).astype(np.float64), ref)
+
+
+# K = 6 and 8: slots sorted in registers, combine fused into the shared
+# expert's down tiles; K = 12 and 20: slots ranked in LDS, stand-alone combine.
+@pytest.mark.parametrize("shared", [False, True], ids=["no_shared", "shared"])
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [6, 12])
+def test_combine_parity(act, K, shared):
+    _combine_case(act, K, shared, seed=5 + K, accumulate="f32")
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["no_shared", "shared"])
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [8, 20])
+def test_combine_layer_accumulator_bitexact(act, K, shared):
+    # same arithmetic in the same order (ascending expert id, a cast after every
+    # addition, the shared output last), so the result is bit-exact
+    _combine_case(act, K, shared, seed=6 + K, accumulate="layer")
 
 
 # ---------------------------------------------------------------------------
