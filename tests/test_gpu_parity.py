@@ -355,15 +355,17 @@ def test_fp8_fused_h_quantisation(name, kw):
     mut[R:] = no_hq(*sargs)
     d = np.abs(got - ref)
     off = d > _bf16_ulp(ref)                       # beyond one bf16 step
-    # one e4m3 step at the value's magnitude (1/8 of it for normal codes) plus
-    # one subnormal code (2^-9 x the block scale, block max / 448): an h within
-    # a few fp32 ulps of zero can round to +1 code on one side and -1 on the other
+    # A gross-error guard: one e4m3 step at the value's magnitude (1/8 of it)
+    # plus 32 subnormal codes (2^-9 x the block scale, block max / 448), i.e.
+    # 1.4e-4 of the block max.  The fp32 sums of the two projections carry an
+    # absolute error of a few 1e-5 of the block max (measured: 2e-5), which
+    # moves an h near zero by several of the small codes around it.
     bmax = np.abs(ref).reshape(ref.shape[0], -1, 128).max(axis=2).repeat(128, axis=1)
     sub = bmax / 448 * 2.0 ** -9
-    step = np.maximum(np.abs(ref) / 8, sub)
-    far = d > (step + sub) * (1 + 2.0 ** -7) + _bf16_ulp(ref)
+    step = np.abs(ref) / 8 + 32 * sub
+    far = d > step * (1 + 2.0 ** -7) + _bf16_ulp(ref)
     off_mut = np.abs(got - mut) > _bf16_ulp(mut)
-    worst = np.argsort((d / (step + sub)).ravel())[-3:]
+    worst = np.argsort((d / step).ravel())[-3:]
     record("fp8_fused_h", case=name, elements=int(got.size), off_by_more_than_bf16_ulp=float(off.mean()),
            beyond_one_e4m3_step=int(far.sum()), vs_unquantised_h=float(off_mut.mean()),
            worst=[[float(got.ravel()[i]), float(ref.ravel()[i]), float(sub.ravel()[i])] for i in worst])
