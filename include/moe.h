@@ -255,6 +255,22 @@ moe_status moe_forward(const moe_params* p, int64_t T, const void* x, const moe_
                        void* y, int32_t* topk_idx, float* topk_w, int32_t* counts,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and result as moe_forward
+ * minus the workspace; the scratch is the library's own device array of
+ * MOE_NOALLOC_SCRATCH_BYTES on each GPU (held until the process ends; its
+ * address is looked up on the first call on a device).  A shape whose
+ * moe_workspace_size() exceeds that returns MOE_ERR_UNSUPPORTED before
+ * anything is enqueued (64 MiB covers the DeepSeek-V3 layer shape up to
+ * about 350 tokens).  Allocates nothing.  Every call on one GPU uses the same
+ * array: calls that may overlap on one GPU (several streams or threads) race
+ * and must be ordered by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_params* p, int64_t T, const void* x,
+                               const moe_weights* w, void* y, int32_t* topk_idx,
+                               float* topk_w, int32_t* counts, void* stream);
+
 /* Kernel timing for benchmarks (not needed to use the layer).
  * moe_profile_start(n) creates n sets of HIP events (host-side objects, no
  * device memory).  While started, each moe_expert_ffn / moe_forward call

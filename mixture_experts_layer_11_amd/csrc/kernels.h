@@ -10,6 +10,9 @@
 namespace moe {
 
 constexpr int kMaxExperts = 512;
+
+// Sets the thread's moe_last_error() text (moe_api.cpp).
+void set_last_error(const char* msg);
 constexpr int kMaxTopk = 32;
 constexpr int kMaxGroups = 64;
 

@@ -269,6 +269,8 @@ moe_status check_weights(const moe_params* p, const moe_weights* w, bool need_ro
 
 }  // namespace
 
+void moe::set_last_error(const char* msg) { g_err = msg; }
+
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }

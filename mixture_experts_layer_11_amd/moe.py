@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         "moe_expert_ffn": (st, [P, i64, _VP, _VP, _VP, W, _VP, _VP, sz, _VP]),
         "moe_combine": (st, [P, i64, _VP, _VP, _VP, _VP, W, _VP, _VP, sz, _VP]),
         "moe_forward": (st, [P, i64, _VP, W, _VP, _VP, _VP, _VP, _VP, sz, _VP]),
+        "moe_forward_noalloc": (st, [P, i64, _VP, W, _VP, _VP, _VP, _VP, _VP]),
         "moe_status_string": (ctypes.c_char_p, [st]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int32, []),
@@ -92,7 +93,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_status_string", "moe_last_error", "moe_abi_version",
+           "moe_forward", "moe_forward_noalloc", "moe_status_string", "moe_last_error", "moe_abi_version",
            "moe_profile_start", "moe_profile_stop", "moe_quant_fp8", "moe_pack_weights",
            "moe_stream_read")
 
@@ -244,6 +245,17 @@ def moe_forward(p: Params, x, w: DeviceWeights, workspace, y=None, topk_idx=None
     _check(lib().moe_forward(ctypes.byref(p.c()), T, _ptr(x), ctypes.byref(cw), _ptr(y),
                              _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
+    return y
+
+
+def moe_forward_noalloc(p: Params, x, w: DeviceWeights, y=None, topk_idx=None, topk_w=None,
+                        counts=None, stream=None):
+    """moe_forward on the library's own device scratch (no workspace argument)."""
+    T = x.shape[0]
+    y = y if y is not None else torch.empty((T, p.dim), dtype=p.act_torch, device=x.device)
+    cw = w.c()
+    _check(lib().moe_forward_noalloc(ctypes.byref(p.c()), T, _ptr(x), ctypes.byref(cw), _ptr(y),
+                                     _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _stream(stream)))
     return y
 
 

@@ -233,3 +233,19 @@ def test_zero_tokens_is_a_noop():
         assert L.moe_forward(ctypes.byref(pc), 0, None, ctypes.byref(w), None, None, None, None,
                              None, 0, None) == moe.MOE_OK
         assert L.moe_gate(ctypes.byref(pc), 0, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_noalloc_limits_checked_before_any_device_work():
+    # the DeepSeek-V3 prefill shape needs far more than the fixed scratch:
+    # refused on the host, naming the limit; T = 0 is a no-op
+    p = _p()
+    L = moe.lib()
+    fake = ctypes.c_void_p(256)
+    w = moe.moe_weights(w_router=256, w1=256, w3=256, w2=256, ws1=256, ws3=256, ws2=256)
+    s = L.moe_forward_noalloc(ctypes.byref(p.c()), 4096, fake, ctypes.byref(w), fake, None, None,
+                              None, None)
+    assert s == moe.MOE_ERR_UNSUPPORTED
+    assert str(64 << 20) in L.moe_last_error().decode()
+    assert L.moe_forward_noalloc(ctypes.byref(p.c()), 0, None, ctypes.byref(w), None, None, None,
+                                 None, None) == moe.MOE_OK
+    assert _ws_status(p, 128)[1] <= 64 << 20      # the decode shape fits
