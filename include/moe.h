@@ -132,10 +132,10 @@ typedef struct moe_params {
  * logical ones and the byte sizes are unchanged.
  * fp8 scales: one fp32 per 128x128 block, [out/128, in/128] per matrix,
  * row-major, stacked over experts for the routed ones; NULL unless
- * weight_dtype is fp8.  Each scale must be a positive normal float (what the
- * amax/448 quantiser produces, 1.0 for an all-zero block); the library reads
- * them only on the device and does not check them, so a zero, subnormal,
- * negative or non-finite scale gives undefined results. */
+ * weight_dtype is fp8.  Each scale must be finite (the library reads them
+ * only on the device and does not check them); a zero scale encodes an
+ * all-zero block whatever its codes.  Each 128-wide K block's partial product
+ * is multiplied by its own scale product, so tiny and zero scales stay exact. */
 typedef struct moe_weights {
   const void* w_router;   /* [E, dim], router_dtype                             */
   const float* bias;      /* [E] fp32 selection bias, or NULL for none          */

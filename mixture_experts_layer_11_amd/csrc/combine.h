@@ -122,28 +122,81 @@ __device__ __forceinline__ void combine8(const CombineArgs& c, int dim, int t, i
   Vec8<T>::store(static_cast<T*>(c.y) + (size_t)t * dim + col, acc);
 }
 
+// The routed sum for one (token, 8 columns) piece, without the store: the
+// token's rows are loaded first (all at once), then summed in ascending row.
+template <typename T, bool kLayer>
+__device__ __forceinline__ void routed8(const CombineArgs& c, int dim, int lo, int hi, int col,
+                                        const int (&rs)[kRegSlots], const float (&ws)[kRegSlots],
+                                        float (&acc)[8]) {
+#pragma clang fp contract(off)
+  const T* out = static_cast<const T*>(c.out);
+  float v[kRegSlots][8];
+#pragma unroll
+  for (int j = 0; j < kRegSlots; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+    if (j < c.topk && rs[j] >= lo && rs[j] < hi) Vec8<T>::load(out + (size_t)rs[j] * dim + col, v[j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRegSlots; ++j) {
+    if (j < c.topk && rs[j] >= lo && rs[j] < hi) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float a = acc[i] + v[j][i] * ws[j];   // two roundings (contract off)
+        acc[i] = kLayer ? to_layer<T>(a) : a;
+      }
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_vals8(const T* sp, float (&s)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if constexpr (sizeof(T) == 2) s[k] = __uint_as_float((uint32_t)sp[k] << 16);
+    else s[k] = sp[k];
+  }
+}
+
 // The fused epilogue of a shared-expert down tile: the tile's shared outputs
 // sit in LDS as layer-dtype values, s_tile[r * ld + j] for token t0 + r and
 // column n0 + j; every thread of the workgroup takes (token, 8-column) pieces,
-// so the routed rows are read as coalesced 16-byte pieces.
+// so the routed rows are read as coalesced 16-byte pieces, two pieces at a
+// time so that 2 x kRegSlots row reads are in flight per thread.
 template <typename T, bool kLayer>
 __device__ __forceinline__ void combine_tile(const CombineArgs& c, const T* s_tile, int ld, int t0,
                                              int rows, int n0, int ncols, int dim) {
+#pragma clang fp contract(off)
   const int chunks = ncols >> 3;
-  for (int i = threadIdx.x; i < rows * chunks; i += blockDim.x) {
-    const int r = i / chunks, cc = i - r * chunks;
-    const int t = t0 + r;
-    int rs[kRegSlots];
-    float ws[kRegSlots];
-    sorted_slots8(c.row_of + (size_t)t * c.topk, c.w + (size_t)t * c.topk, c.topk, rs, ws);
-    float s[8];
-    const T* sp = s_tile + r * ld + 8 * cc;
+  const int items = rows * chunks;
+  const int lo = c.offsets != nullptr ? c.offsets[c.e_begin] : 0;
+  const int hi = c.offsets != nullptr ? c.offsets[c.e_end] : 0x7fffffff;
+  const int step = blockDim.x;
+  for (int i = threadIdx.x; i < items; i += 2 * step) {
+    const int i2 = i + step;
+    const bool two = i2 < items;
+    const int ra = i / chunks, ca = i - ra * chunks;
+    const int ib = two ? i2 : i;
+    const int rb = ib / chunks, cb = ib - rb * chunks;
+    int rsa[kRegSlots], rsb[kRegSlots];
+    float wsa[kRegSlots], wsb[kRegSlots];
+    sorted_slots8(c.row_of + (size_t)(t0 + ra) * c.topk, c.w + (size_t)(t0 + ra) * c.topk, c.topk, rsa, wsa);
+    sorted_slots8(c.row_of + (size_t)(t0 + rb) * c.topk, c.w + (size_t)(t0 + rb) * c.topk, c.topk, rsb, wsb);
+    float acc_a[8], acc_b[8];
+    routed8<T, kLayer>(c, dim, lo, hi, n0 + 8 * ca, rsa, wsa, acc_a);
+    routed8<T, kLayer>(c, dim, lo, hi, n0 + 8 * cb, rsb, wsb, acc_b);
+    float sa[8], sb[8];
+    lds_vals8<T>(s_tile + ra * ld + 8 * ca, sa);
+    lds_vals8<T>(s_tile + rb * ld + 8 * cb, sb);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if constexpr (sizeof(T) == 2) s[k] = __uint_as_float((uint32_t)sp[k] << 16);
-      else s[k] = sp[k];
+      acc_a[k] = acc_a[k] + sa[k];
+      acc_b[k] = acc_b[k] + sb[k];
     }
-    combine8<T, kLayer>(c, dim, t, n0 + 8 * cc, rs, ws, s);
+    Vec8<T>::store(static_cast<T*>(c.y) + (size_t)(t0 + ra) * dim + n0 + 8 * ca, acc_a);
+    if (two) Vec8<T>::store(static_cast<T*>(c.y) + (size_t)(t0 + rb) * dim + n0 + 8 * cb, acc_b);
   }
 }
 

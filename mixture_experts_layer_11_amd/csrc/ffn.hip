@@ -32,7 +32,8 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __res
                                                             int E, int ntok, int routed,
                                                             int shared_up, int shared_down,
                                                             int bm, int nt_up, int nt_up_s,
-                                                            int nt_dn, int e_begin, int e_end,
+                                                            int nt_dn, int bm_s, int e_begin,
+                                                            int e_end,
                                                             int32_t* __restrict__ sched) {
   __shared__ int sc[3][1024];
   const int g = threadIdx.x;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __res
     const int mt = (ntok + bm - 1) / bm;
     c[0] = shared_up ? mt * nt_up_s : 0;
     c[1] = shared_down == 1 ? mt * nt_dn : 0;
-    c[2] = shared_down == 2 ? mt * nt_dn : 0;
+    c[2] = shared_down == 2 ? (ntok + bm_s - 1) / bm_s * nt_dn : 0;
   }
 #pragma unroll
   for (int s = 0; s < 3; ++s) sc[s][g] = c[s];
@@ -363,6 +364,12 @@ using SMid = SCfg<64, 8, 4, 2, 4, 2, true>;
 // 32-64 rows per expert: an expert fills one m-tile, so each weight slice is
 // read about once
 using SBigNT = SCfg<128, 8, 4, 3, 4, 2, true>;
+// The shared expert's down tiles fused with the combine (one launch of T
+// rows): every m-tile reads the same weight slices, so ordinary loads.
+#ifndef MOE_COMB_BM
+#define MOE_COMB_BM 128
+#endif
+using SComb = SCfg<MOE_COMB_BM, 8, 4, (MOE_COMB_BM >= 128 ? 3 : 2), 4, 2, false>;
 
 template <class C>
 struct StreamSrc {
@@ -597,12 +604,13 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
 // row l%32, bytes 32*(l/32)..+31 of a 64-byte K half; B likewise for the token
 // row; D as the bf16 32x32 tile, so D elements i < 8 are W1 rows (or the
 // first 16 W2 rows) and i >= 8 the W3 rows.  Two MFMAs per 128-wide K block.
-// Block scales: the accumulator is kept in units of the current block's
-// scale s = w_scale * a_scale (one s per half of the elements): each block
-// does acc <- mfma(W, X, acc * s_prev / s) and the result is acc * s_last, the
-// same sum as sum_kb s_kb * (W_kb X_kb) up to one fp32 rounding per block,
-// with no partial-product registers.  Token slices carry their per-row
-// activation scale into LDS.  The 32-row fragment pattern reads LDS without
+// Block scales ("promotion"): each block's two MFMAs go into a fresh partial
+// product P, then acc += s * P with s = w_scale * a_scale (one s per half of
+// the elements): sum_kb s_kb * (W_kb X_kb) in fp32, with no reciprocal, so a
+// zero or tiny scale stays exact and nothing overflows.  P is double-buffered
+// across sub-tiles: the promotion of sub-tile a-1 is issued after the MFMAs
+// of sub-tile a, so it never waits for them.  Token slices carry their
+// per-row activation scale into LDS.  The 32-row fragment pattern reads LDS without
 // bank conflicts (a 16x16x128 pattern conflicts on half its cycles), and 192
 // tokens cover most experts of an 8192-token batch in two m-tiles.  The up
 // epilogue quantises h per 1x128 block: the 8 waves' 16-column slices of a
@@ -621,7 +629,7 @@ struct StreamSrcF8 {
 };
 
 template <int MT, bool kNT>
-__device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], float2 (&sxs)[F8::NB][F8::BM],
+__device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], float (&sxs)[F8::NB][F8::BM],
                                                   const StreamSrcF8& S, int nk,
                                                   f32x16_t (&acc)[kF8MT]) {
   constexpr int XL = std::min(F8::XLOADS, (32 * MT + F8::ROWS_PER_PASS - 1) / F8::ROWS_PER_PASS);
@@ -633,9 +641,6 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
   float wsc[RING][2];            // [slice % RING][D half]
   uint4 xr[XD][F8::XLOADS];      // token slices between load and LDS store: [slice % XD]
   float xsr[XD][F8::XLOADS];
-  float sprev[MT][2];            // units of the accumulator halves
-#pragma unroll
-  for (int a = 0; a < MT; ++a) sprev[a][0] = sprev[a][1] = 1.f;
   auto wload = [&](i32x8_t_ (&dst)[2], float (&sc)[2], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
@@ -660,8 +665,7 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
     for (int i = 0; i < XL; ++i) {
       static_assert(F8::BM % F8::ROWS_PER_PASS == 0, "every token load pass lands inside the tile");
       *reinterpret_cast<uint4*>(&sx[buf][S.lds_st + F8::ROWS_PER_PASS * i * F8::STRIDE]) = src[i];
-      // (scale, 1/scale), equal values from the row's 8 lanes
-      sxs[buf][(threadIdx.x >> 3) + F8::ROWS_PER_PASS * i] = make_float2(sc[i], __builtin_amdgcn_rcpf(sc[i]));
+      sxs[buf][(threadIdx.x >> 3) + F8::ROWS_PER_PASS * i] = sc[i];   // equal values from the row's 8 lanes
     }
   };
   // the token staging of the bf16 stream loop: slice j in LDS buffer j % NB,
@@ -684,38 +688,39 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
     wload(wr[(ws + RING - 1) % RING], wsc[(ws + RING - 1) % RING], kt + RING - 1);
     __builtin_amdgcn_sched_barrier(0);
     const char* sb = sx[kt % NB] + fr * F8::STRIDE + 32 * fg;
-    const float2* sbs = sxs[kt % NB] + fr;
-    const float iw[2] = {__builtin_amdgcn_rcpf(wsc[ws][0]), __builtin_amdgcn_rcpf(wsc[ws][1])};
-    // the fragments and scales of sub-tile a+1 are read from LDS while
-    // sub-tile a is rescaled and multiplied
+    const float* sbs = sxs[kt % NB] + fr;
+    // the fragments and scale of sub-tile a+1 are read from LDS while
+    // sub-tile a is multiplied; the promotion of sub-tile a-1 follows the
+    // MFMAs of sub-tile a, so it never waits for them
     i32x8_t_ bx[2][2];
-    float2 xsc[2];
+    float xsc[2];
+    f32x16_t part[2];              // partial products of the block, sub-tiles a-1 and a
     auto frag = [&](int a, int b) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) bx[b][j] = *reinterpret_cast<const i32x8_t_*>(sb + 32 * a * F8::STRIDE + 64 * j);
       xsc[b] = sbs[32 * a];
     };
+    // acc += s * partial with s = w_scale * a_scale, one s per half of D
+    auto promote = [&](int a, float as) {
+      const float s0 = wsc[ws][0] * as, s1 = wsc[ws][1] * as;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][i] = fmaf(part[a & 1][i], i < 8 ? s0 : s1, acc[a][i]);
+    };
     frag(0, 0);
+    float as_prev = 0.f;
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
       if (a + 1 < MT) frag(a + 1, (a + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      const float2 xs = xsc[a & 1];
-      float ratio[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {   // s_prev / s with s = w_scale * a_scale
-        ratio[h] = sprev[a][h] * iw[h] * xs.y;
-        sprev[a][h] = wsc[ws][h] * xs.x;
-      }
-      f32x16_t c = acc[a];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] *= ratio[i >> 3];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][j], bx[a & 1][j], c, 0, 0, 0, 127, 0, 127);
-      acc[a] = c;
+      const float as = xsc[a & 1];
+      const f32x16_t zero = {};
+      f32x16_t c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][0], bx[a & 1][0], zero, 0, 0, 0, 127, 0, 127);
+      part[a & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][1], bx[a & 1][1], c, 0, 0, 0, 127, 0, 127);
+      if (a > 0) promote(a - 1, as_prev);
+      as_prev = as;
       __builtin_amdgcn_sched_barrier(0);
     }
+    promote(MT - 1, as_prev);
     xstore(xr[(r + D) % XD], xsr[(r + D) % XD], (kt + D) % NB);
     if (r % D == D - 1) __syncthreads();
   };
@@ -729,17 +734,13 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
     for (; kt < nmain; kt += UNROLL) body(kt, std::integral_constant<int, I>{}...);
     tail(kt, std::integral_constant<int, I>{}...);
   }(std::make_integer_sequence<int, UNROLL>{});
-#pragma unroll
-  for (int a = 0; a < MT; ++a)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[a][i] *= sprev[a][i >> 3];
 }
 
 template <bool kUp, bool kNT, bool kComb = false>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_fp8_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[F8::NB][F8::LDS];
-  __shared__ float2 sxs[F8::NB][F8::BM];
+  __shared__ float sxs[F8::NB][F8::BM];
   __shared__ float wamax[kUp ? F8::WAVES : 1][F8::BM];
   static_assert(!kComb || F8::BM * comb_ld<F8::BM, F8::BN>() * 2 <= F8::NB * F8::LDS,
                 "the combine tile fits in the token buffers");
@@ -1160,6 +1161,7 @@ struct FfnPlan {
   Tiles t;
   bool nt;              // stream tiles read their weights non-temporally
   int bm, nt_up, nt_up_s, nt_dn, threads;
+  int bm_s, threads_s;       // tile rows and threads of the shared down + combine launch
   long g_up, g_dn, g_dn_s;   // workgroups (multiples of 8): up, down, shared down + combine
 };
 
@@ -1185,18 +1187,22 @@ static FfnPlan plan_ffn(const FfnProblem& p) {
   L.nt_up = ceil_div(p.inter, bn_up);
   L.nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
   L.nt_dn = ceil_div(p.dim, bn_dn);
+  // the bf16 stream kinds fuse the combine on SComb tiles (same 256 columns)
+  const bool comb_cfg = !f8 && L.t != Tiles::Skinny;
+  L.bm_s = comb_cfg ? SComb::BM : L.bm;
+  L.threads_s = comb_cfg ? SComb::THREADS : L.threads;
   const long Rr = p.routed ? R : 0;
   L.g_up = Rr || p.shared_up ? round8(max_tiles(Rr, p.E, p.ntok, p.shared_up, L.bm, L.nt_up, L.nt_up_s)) : 0;
   const bool dn_store = p.shared_down == SharedDown::Store;
   L.g_dn = Rr || dn_store ? round8(max_tiles(Rr, p.E, p.ntok, dn_store, L.bm, L.nt_dn, L.nt_dn)) : 0;
-  L.g_dn_s = p.shared_down == SharedDown::Combine ? round8((long)ceil_div(p.ntok, L.bm) * L.nt_dn) : 0;
+  L.g_dn_s = p.shared_down == SharedDown::Combine ? round8((long)ceil_div(p.ntok, L.bm_s) * L.nt_dn) : 0;
   return L;
 }
 
 static long quant_blocks(int ntok, int dim) { return ((long)ntok * (dim / 128) * 16 + 255) / 256; }
 
 static long plan_items(const FfnProblem& p, const FfnPlan& L) {
-  long items = std::max(std::max(L.g_up, L.g_dn), L.g_dn_s) * L.threads;
+  long items = std::max(std::max(L.g_up, L.g_dn) * L.threads, L.g_dn_s * L.threads_s);
   if (p.wkind == WKind::FP8) items = std::max(items, quant_blocks(p.ntok, p.dim) * 256);
   return items;
 }
@@ -1221,13 +1227,14 @@ static void launch_down(const FfnProblem& q, const FfnPlan& L, int grid, hipStre
   const bool f8 = q.wkind == WKind::FP8, nt = L.nt;
   if (t == Tiles::Big && f8 && nt) stream_fp8_kernel<false, true, kComb><<<grid, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big && f8) stream_fp8_kernel<false, false, kComb><<<grid, F8::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false, kComb><<<grid, SHuge::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false, kComb><<<grid, SBigNT::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big) stream_bf16_kernel<SBig, false, kComb><<<grid, SBig::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Mid) stream_bf16_kernel<SMid, false, kComb><<<grid, SMid::THREADS, 0, st>>>(q);
   else if (f8) down_skinny_fp8_kernel<kComb><<<grid, 256, 0, st>>>(q);
-  else if (q.wkind == WKind::BF16) down_skinny_kernel<uint16_t, kComb><<<grid, 256, 0, st>>>(q);
-  else down_skinny_kernel<float, kComb><<<grid, 256, 0, st>>>(q);
+  else if (t == Tiles::Skinny && q.wkind == WKind::BF16) down_skinny_kernel<uint16_t, kComb><<<grid, 256, 0, st>>>(q);
+  else if (t == Tiles::Skinny) down_skinny_kernel<float, kComb><<<grid, 256, 0, st>>>(q);
+  else if constexpr (kComb) stream_bf16_kernel<SComb, false, true><<<grid, SComb::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, false, false><<<grid, SHuge::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, false, false><<<grid, SBigNT::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<SBig, false, false><<<grid, SBig::THREADS, 0, st>>>(q);
+  else stream_bf16_kernel<SMid, false, false><<<grid, SMid::THREADS, 0, st>>>(q);
 }
 
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
@@ -1239,7 +1246,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.routed ? p.offsets : nullptr, p.E, p.ntok,
                                           p.routed ? 1 : 0, p.shared_up ? 1 : 0,
                                           (int)p.shared_down, L.bm, L.nt_up, L.nt_up_s, L.nt_dn,
-                                          p.e_begin, p.e_end, p.sched);
+                                          L.bm_s, p.e_begin, p.e_end, p.sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const FfnProblem& q = p;

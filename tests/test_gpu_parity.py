@@ -374,6 +374,31 @@ def test_fp8_fused_h_quantisation(name, kw):
     assert off_mut.mean() >= 0.3
 
 
+# Extreme block scales in the fp8 stream tiles: a 1x128 activation block of
+# values near 1e-36 (its scale is near 2e-39, a subnormal fp32) and 128x128
+# weight blocks whose scale is 0 (the block then encodes zeros whatever its
+# codes).  Every block's partial product is promoted with its own
+# w_scale * a_scale, so the result stays finite and matches the oracle.
+
+@pytest.mark.parametrize("T,topk", [(700, 2), (16, 4)], ids=["stream", "skinny"])
+def test_fp8_tiny_and_zero_block_scales(T, topk):
+    cfg = tiny_cfg(f"fp8_extreme_T{T}", T=T, E=8, n_groups=2, topk_groups=1, topk=topk,
+                   dim=256, inter=256, inter_shared=256, act_dtype="bf16", router_dtype="bf16",
+                   w_dtype="fp8", seed=5151)
+    layer = inputs.draw_layer(cfg)
+    xv = inputs.bf16_bits_to_f32(layer.x)
+    xv[5, :128] *= np.float32(1e-36)
+    xv[6, 128:] *= np.float32(1e-30)
+    layer.x = inputs.f32_to_bf16_bits(xv)
+    for e in range(cfg.E):
+        layer.w1_s[e, 0, 0] = 0.0          # W1 rows 0-127 x K block 0
+        layer.w2_s[e, 1, 1] = 0.0          # W2 rows 128-255 x K block 1
+    layer.shared.w3_s[1, 0] = 0.0
+    dw = moe.upload_layer(layer)
+    y, same = forward_and_check(cfg, layer, dw)
+    assert torch.isfinite(y.float()).all()
+
+
 # ---------------------------------------------------------------------------
 # fp8 activation quantiser (bit-exact codes and scales)
 # ---------------------------------------------------------------------------
