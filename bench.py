@@ -101,9 +101,10 @@ def workload_numbers(cfg, counts, experts=None):
     routed_rows = int(counts.sum())                         # T * K for the full range
     flops = 2 * T * E * dim + 2 * routed_rows * 3 * dim * I + 2 * T * 3 * dim * Is
     bytes_ = active * per_expert + shared + E * dim * rsz + T * dim * asz * 2
-    hsz = 1 if cfg.w_dtype == "fp8" else asz
-    up_bytes = (active * 2 * (I * dim * wsz + scale_b) + 2 * (Is * dim * wsz) + T * dim * asz
-                + (routed_rows * I + T * Is) * hsz)
+    shared_scale_b = 4 * (dim // 128) * (Is // 128) if cfg.w_dtype == "fp8" else 0
+    # up launch: W1 and W3 of the active experts and of the shared expert, x read
+    # once (h is an intermediate buffer: not algorithmic)
+    up_bytes = active * 2 * (I * dim * wsz + scale_b) + 2 * (Is * dim * wsz + shared_scale_b) + T * dim * asz
     up_flops = 2 * routed_rows * 2 * dim * I + 2 * T * 2 * dim * Is
     return dict(active_experts=active, flops=flops, bytes=bytes_, up_bytes=up_bytes,
                 up_flops=up_flops, per_expert_up_bytes=2 * (I * dim * wsz + scale_b))

@@ -50,6 +50,23 @@ def test_counts_match_per_matrix_sums(name):
     assert r["active_experts"] == int((counts > 0).sum())
 
 
+@pytest.mark.parametrize("name", [c.name for c in inputs.CONFIGS])
+def test_up_launch_bytes_are_w1_w3_and_x(name):
+    """The up launch's algorithmic bytes: W1 and W3 of every expert that gets
+    rows, the shared W1 and W3, and x; no intermediate buffer."""
+    cfg = inputs.config_by_name(name)
+    counts = np.random.default_rng(2).multinomial(cfg.T * cfg.topk, np.ones(cfg.E) / cfg.E)
+    counts[:2] = 0
+    counts[2] += cfg.T * cfg.topk - counts.sum()
+    wsz = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.w_dtype]
+    asz = 4 if cfg.act_dtype == "f32" else 2
+    want = cfg.T * cfg.dim * asz
+    mats = [(cfg.inter, cfg.dim)] * 2 * int((counts > 0).sum()) + [(cfg.inter_shared, cfg.dim)] * 2
+    for rows, cols in mats:
+        want += rows * cols * wsz + (4 * (rows // 128) * (cols // 128) if cfg.w_dtype == "fp8" else 0)
+    assert bench.workload_numbers(cfg, counts)["up_bytes"] == want
+
+
 @pytest.mark.parametrize("name,tflop,gbytes", [
     ("c2_dsv3_prefill_T4096", 3.262, 22.76),
     ("c3_skewed_softmax_T8192", 1.136, 1.21),
