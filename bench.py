@@ -110,7 +110,7 @@ def workload_numbers(cfg, counts, experts=None):
                 up_flops=up_flops, per_expert_up_bytes=2 * (I * dim * wsz + scale_b))
 
 
-KERNEL_SOURCES = ("ffn.hip", "common.h", "kernels.h")   # what the expert kernels are built from
+KERNEL_SOURCES = ("ffn.hip", "common.h", "kernels.h", "combine.h")   # what the expert kernels are built from
 
 
 def kernel_source_sha():
