@@ -21,8 +21,10 @@ namespace moe {
 
 template <typename T> struct Vec8;
 template <> struct Vec8<uint16_t> {
-  __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+  using Raw = uint4;   // 8 values as loaded
+  __device__ __forceinline__ static Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static Raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ static void unpack(const Raw& u, float (&v)[8]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -30,6 +32,7 @@ template <> struct Vec8<uint16_t> {
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
+  __device__ __forceinline__ static void load(const uint16_t* p, float (&v)[8]) { unpack(load_raw(p), v); }
   __device__ __forceinline__ static void store(uint16_t* p, const float (&v)[8]) {
     uint4 u;
     u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
@@ -40,11 +43,17 @@ template <> struct Vec8<uint16_t> {
   }
 };
 template <> struct Vec8<float> {
-  __device__ __forceinline__ static void load(const float* p, float (&v)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  struct Raw { float4 a, b; };
+  __device__ __forceinline__ static Raw load_raw(const float* p) {
+    return Raw{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
   }
+  __device__ __forceinline__ static Raw zero() {
+    return Raw{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  }
+  __device__ __forceinline__ static void unpack(const Raw& u, float (&v)[8]) {
+    v[0] = u.a.x; v[1] = u.a.y; v[2] = u.a.z; v[3] = u.a.w; v[4] = u.b.x; v[5] = u.b.y; v[6] = u.b.z; v[7] = u.b.w;
+  }
+  __device__ __forceinline__ static void load(const float* p, float (&v)[8]) { unpack(load_raw(p), v); }
   __device__ __forceinline__ static void store(float* p, const float (&v)[8]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -122,33 +131,55 @@ __device__ __forceinline__ void combine8(const CombineArgs& c, int dim, int t, i
   Vec8<T>::store(static_cast<T*>(c.y) + (size_t)t * dim + col, acc);
 }
 
-// The routed sum for one (token, 8 columns) piece, without the store: the
-// token's rows are loaded first (all at once), then summed in ascending row.
-template <typename T, bool kLayer>
-__device__ __forceinline__ void routed8(const CombineArgs& c, int dim, int lo, int hi, int col,
-                                        const int (&rs)[kRegSlots], const float (&ws)[kRegSlots],
-                                        float (&acc)[8]) {
-#pragma clang fp contract(off)
-  const T* out = static_cast<const T*>(c.out);
-  float v[kRegSlots][8];
+// The routing of a combine tile's tokens, staged in LDS: kRegSlots slots per
+// token in ascending row, rows that do not count (past topk, or outside the
+// expert range) marked kNoRow so they sort last and are skipped.
+constexpr int32_t kNoRow = 0x7fffffff;
+struct __attribute__((aligned(8))) Slot {
+  int32_t row;
+  float w;
+};
+
+// A token's raw routing (row_of and weights) in registers, loaded by thread r
+// of the workgroup for token t0 + r; stored to LDS sorted by slots_store.
+struct SlotLoad {
+  int32_t r[kRegSlots];
+  float w[kRegSlots];
+};
+
+__device__ __forceinline__ void slots_issue(const CombineArgs& c, int t0, int rows, SlotLoad& L) {
+  const int r = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < kRegSlots; ++j) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
-    if (j < c.topk && rs[j] >= lo && rs[j] < hi) Vec8<T>::load(out + (size_t)rs[j] * dim + col, v[j]);
+  for (int k = 0; k < kRegSlots; ++k) {
+    const bool ld = r < rows && k < c.topk;
+    L.r[k] = ld ? c.row_of[(size_t)(t0 + r) * c.topk + k] : kNoRow;
+    L.w[k] = ld ? c.w[(size_t)(t0 + r) * c.topk + k] : 0.f;
   }
+}
+
+// Sort thread r's slots by row (a fully unrolled exchange network) and store
+// them as token r's LDS slots; the caller's next workgroup barrier publishes
+// them.  Requires rows <= blockDim.x.
+__device__ __forceinline__ void slots_store(const CombineArgs& c, int rows, SlotLoad L, Slot* slots) {
+  const int r = threadIdx.x;
+  if (r >= rows) return;
+  const int lo = c.offsets != nullptr ? c.offsets[c.e_begin] : 0;
+  const int hi = c.offsets != nullptr ? c.offsets[c.e_end] : kNoRow;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int k = 0; k < kRegSlots; ++k)
+    if (L.r[k] < lo || L.r[k] >= hi) L.r[k] = kNoRow;
 #pragma unroll
-  for (int j = 0; j < kRegSlots; ++j) {
-    if (j < c.topk && rs[j] >= lo && rs[j] < hi) {
+  for (int i = 0; i < kRegSlots; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float a = acc[i] + v[j][i] * ws[j];   // two roundings (contract off)
-        acc[i] = kLayer ? to_layer<T>(a) : a;
+    for (int j = i + 1; j < kRegSlots; ++j)
+      if (L.r[j] < L.r[i]) {
+        const int tr = L.r[i]; L.r[i] = L.r[j]; L.r[j] = tr;
+        const float tw = L.w[i]; L.w[i] = L.w[j]; L.w[j] = tw;
       }
-    }
-  }
+  int4* d = reinterpret_cast<int4*>(slots + r * kRegSlots);
+#pragma unroll
+  for (int k = 0; k < kRegSlots; k += 2)
+    d[k / 2] = make_int4(L.r[k], __float_as_int(L.w[k]), L.r[k + 1], __float_as_int(L.w[k + 1]));
 }
 
 template <typename T>
@@ -162,41 +193,71 @@ __device__ __forceinline__ void lds_vals8(const T* sp, float (&s)[8]) {
 
 // The fused epilogue of a shared-expert down tile: the tile's shared outputs
 // sit in LDS as layer-dtype values, s_tile[r * ld + j] for token t0 + r and
-// column n0 + j; every thread of the workgroup takes (token, 8-column) pieces,
-// so the routed rows are read as coalesced 16-byte pieces, two pieces at a
-// time so that 2 x kRegSlots row reads are in flight per thread.
-template <typename T, bool kLayer>
-__device__ __forceinline__ void combine_tile(const CombineArgs& c, const T* s_tile, int ld, int t0,
-                                             int rows, int n0, int ncols, int dim) {
+// column n0 + j, and the tokens' sorted slots in LDS (slots_store).  Every
+// thread of the workgroup takes (token, 8-column) pieces, NP at a time: the
+// routed rows of all NP pieces are loaded first (NP x kRegSlots coalesced
+// 16-byte reads in flight per thread), then each piece is summed in ascending
+// row, its shared value added last, and stored.
+template <typename T, bool kLayer, int NP>
+__device__ __forceinline__ void combine_tile(const CombineArgs& c, const Slot* slots, const T* s_tile, int ld,
+                                             int t0, int rows, int n0, int ncols, int dim) {
 #pragma clang fp contract(off)
   const int chunks = ncols >> 3;
   const int items = rows * chunks;
-  const int lo = c.offsets != nullptr ? c.offsets[c.e_begin] : 0;
-  const int hi = c.offsets != nullptr ? c.offsets[c.e_end] : 0x7fffffff;
   const int step = blockDim.x;
-  for (int i = threadIdx.x; i < items; i += 2 * step) {
-    const int i2 = i + step;
-    const bool two = i2 < items;
-    const int ra = i / chunks, ca = i - ra * chunks;
-    const int ib = two ? i2 : i;
-    const int rb = ib / chunks, cb = ib - rb * chunks;
-    int rsa[kRegSlots], rsb[kRegSlots];
-    float wsa[kRegSlots], wsb[kRegSlots];
-    sorted_slots8(c.row_of + (size_t)(t0 + ra) * c.topk, c.w + (size_t)(t0 + ra) * c.topk, c.topk, rsa, wsa);
-    sorted_slots8(c.row_of + (size_t)(t0 + rb) * c.topk, c.w + (size_t)(t0 + rb) * c.topk, c.topk, rsb, wsb);
-    float acc_a[8], acc_b[8];
-    routed8<T, kLayer>(c, dim, lo, hi, n0 + 8 * ca, rsa, wsa, acc_a);
-    routed8<T, kLayer>(c, dim, lo, hi, n0 + 8 * cb, rsb, wsb, acc_b);
-    float sa[8], sb[8];
-    lds_vals8<T>(s_tile + ra * ld + 8 * ca, sa);
-    lds_vals8<T>(s_tile + rb * ld + 8 * cb, sb);
+  const T* out = static_cast<const T*>(c.out);
+  for (int i0 = threadIdx.x; i0 < items; i0 += NP * step) {
+    int pr[NP], pc[NP];
+    uint32_t used[NP];            // bit k: slot k holds a routed row of the sum
+    float ws[NP][kRegSlots];
+    typename Vec8<T>::Raw v[NP][kRegSlots];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      acc_a[k] = acc_a[k] + sa[k];
-      acc_b[k] = acc_b[k] + sb[k];
+    for (int q = 0; q < NP; ++q) {
+      const int i = i0 + q * step;
+      const bool live = i < items;
+      const int ii = live ? i : i0;
+      pr[q] = ii / chunks;
+      pc[q] = ii - pr[q] * chunks;
+      used[q] = 0u;
+      const int4* sl = reinterpret_cast<const int4*>(slots + pr[q] * kRegSlots);
+#pragma unroll
+      for (int k = 0; k < kRegSlots; k += 2) {
+        const int4 e = sl[k / 2];
+        const int rr[2] = {e.x, e.z};
+        ws[q][k] = __int_as_float(e.y);
+        ws[q][k + 1] = __int_as_float(e.w);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (live && rr[h] != kNoRow) {
+            v[q][k + h] = Vec8<T>::load_raw(out + (size_t)rr[h] * dim + n0 + 8 * pc[q]);
+            used[q] |= 1u << (k + h);
+          } else {
+            v[q][k + h] = Vec8<T>::zero();
+          }
+        }
+      }
     }
-    Vec8<T>::store(static_cast<T*>(c.y) + (size_t)(t0 + ra) * dim + n0 + 8 * ca, acc_a);
-    if (two) Vec8<T>::store(static_cast<T*>(c.y) + (size_t)(t0 + rb) * dim + n0 + 8 * cb, acc_b);
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      if (i0 + q * step >= items) continue;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kRegSlots; ++k) {
+        if (!(used[q] & (1u << k))) continue;
+        float x[8];
+        Vec8<T>::unpack(v[q][k], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = acc[e] + x[e] * ws[q][k];   // two roundings (contract off)
+          acc[e] = kLayer ? to_layer<T>(a) : a;
+        }
+      }
+      float sv[8];
+      lds_vals8<T>(s_tile + pr[q] * ld + 8 * pc[q], sv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + sv[e];
+      Vec8<T>::store(static_cast<T*>(c.y) + (size_t)(t0 + pr[q]) * dim + n0 + 8 * pc[q], acc);
+    }
   }
 }
 

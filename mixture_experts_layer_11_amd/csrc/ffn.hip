@@ -237,14 +237,14 @@ __global__ __launch_bounds__(256) void up_skinny_kernel(FfnProblem p) {
 // The fused combine of a shared-expert down tile: the tile's outputs go to
 // LDS rounded to the layer dtype (the shared module's output), then the whole
 // workgroup forms y for the tile's tokens and columns (combine.h).
-template <typename T>
-__device__ __forceinline__ void combine_from_lds(const FfnProblem& p, const T* s_tile, int ld,
-                                                 const TileInfo& ti, int n0, int bn) {
+template <typename T, int NP>
+__device__ __forceinline__ void combine_from_lds(const FfnProblem& p, const Slot* slots, const T* s_tile,
+                                                 int ld, const TileInfo& ti, int n0, int bn) {
   const int ncols = min(bn, p.dim - n0);
   if (p.comb.layer_acc)
-    combine_tile<T, true>(p.comb, s_tile, ld, ti.m0, ti.mrows, n0, ncols, p.dim);
+    combine_tile<T, true, NP>(p.comb, slots, s_tile, ld, ti.m0, ti.mrows, n0, ncols, p.dim);
   else
-    combine_tile<T, false>(p.comb, s_tile, ld, ti.m0, ti.mrows, n0, ncols, p.dim);
+    combine_tile<T, false, NP>(p.comb, slots, s_tile, ld, ti.m0, ti.mrows, n0, ncols, p.dim);
 }
 
 // kComb: the launch holds only the shared expert's tiles, and each ends with
@@ -253,9 +253,12 @@ template <typename T, bool kComb>
 __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
   constexpr int LD = kDnBN + 8;                     // LDS row of the combine tile (elements)
   __shared__ __attribute__((aligned(16))) T s_tile[kComb ? 16 * LD : 1];
+  __shared__ __attribute__((aligned(16))) Slot slots[kComb ? 16 * kRegSlots : 1];
   TileInfo ti;
   const int32_t* sched = p.sched + (kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, ti)) return;
+  SlotLoad sl;                                      // the tokens' routing, loaded under the K loop
+  if constexpr (kComb) slots_issue(p.comb, ti.m0, ti.mrows, sl);
   const bool shared = ti.g == p.E;
   const int K = shared ? p.inter_s : p.inter;
   const int N = p.dim;
@@ -291,8 +294,9 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
           else *d = v;
         }
     }
+    slots_store(p.comb, ti.mrows, sl, slots);
     __syncthreads();
-    combine_from_lds<T>(p, s_tile, LD, ti, ti.nt * kDnBN, kDnBN);
+    combine_from_lds<T, 1>(p, slots, s_tile, LD, ti, ti.nt * kDnBN, kDnBN);
     return;
   }
   if (r < ti.mrows) {
@@ -473,12 +477,15 @@ template <int BM, int BN>
 constexpr int comb_ld() { return BN + 8; }
 
 template <class C, bool kUp, bool kComb = false>
-__device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::LDS]) {
+__device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::LDS], Slot* slots) {
   static_assert(!kComb || C::BM * comb_ld<C::BM, C::BN>() * 2 <= C::NB * C::LDS,
                 "the combine tile fits in the token buffers");
   TileInfo ti;
   const int32_t* sched = p.sched + (kUp ? 0 : kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, C::BM, ti)) return;
+  static_assert(!kComb || C::BM <= C::THREADS, "one thread stages each token's slots");
+  SlotLoad sl;                                      // the tokens' routing, loaded under the K loop
+  if constexpr (kComb) slots_issue(p.comb, ti.m0, ti.mrows, sl);
   const bool shared = ti.g == p.E;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter);
@@ -546,6 +553,7 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
   if constexpr (kComb) {
     constexpr int LD = comb_ld<C::BM, C::BN>();
     uint16_t* st = reinterpret_cast<uint16_t*>(&sx[0][0]);
+    slots_store(p.comb, rows_left, sl, slots);
     __syncthreads();                  // every wave is done with the token buffers
     if (wave_active) {
       const int ml = lane & 31, rg = 4 * (lane >> 5);
@@ -563,7 +571,7 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
       }
     }
     __syncthreads();
-    combine_from_lds<uint16_t>(p, st, LD, ti, ti.nt * C::BN, C::BN);
+    combine_from_lds<uint16_t, 4>(p, slots, st, LD, ti, ti.nt * C::BN, C::BN);
     return;
   }
   if (!wave_active) return;
@@ -742,8 +750,10 @@ void stream_fp8_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[F8::NB][F8::LDS];
   __shared__ float sxs[F8::NB][F8::BM];
   __shared__ float wamax[kUp ? F8::WAVES : 1][F8::BM];
+  __shared__ __attribute__((aligned(16))) Slot slots[kComb ? F8::BM * kRegSlots : 1];
   static_assert(!kComb || F8::BM * comb_ld<F8::BM, F8::BN>() * 2 <= F8::NB * F8::LDS,
                 "the combine tile fits in the token buffers");
+  static_assert(!kComb || F8::BM <= F8::THREADS, "one thread stages each token's slots");
   TileInfo ti;
   const int32_t* sched = p.sched + (kUp ? 0 : kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, F8::BM, ti)) return;
@@ -850,6 +860,12 @@ void stream_fp8_kernel(FfnProblem p) {
   } else if constexpr (kComb) {
     constexpr int LD = comb_ld<F8::BM, F8::BN>();
     uint16_t* st = reinterpret_cast<uint16_t*>(&sx[0][0]);
+    {
+      // the tokens' routing (loaded here: the K loop has no registers to spare)
+      SlotLoad sl;
+      slots_issue(p.comb, ti.m0, ti.mrows, sl);
+      slots_store(p.comb, ti.mrows, sl, slots);
+    }
     __syncthreads();                  // every wave is done with the token buffers
     if (wave_active) {
 #pragma unroll
@@ -866,7 +882,7 @@ void stream_fp8_kernel(FfnProblem p) {
       }
     }
     __syncthreads();
-    combine_from_lds<uint16_t>(p, st, LD, ti, ti.nt * F8::BN, F8::BN);
+    combine_from_lds<uint16_t, 4>(p, slots, st, LD, ti, ti.nt * F8::BN, F8::BN);
   } else {
     if (!wave_active) return;
 #pragma unroll
@@ -888,7 +904,8 @@ template <class C, bool kUp, bool kComb = false>
 __global__ __launch_bounds__(C::THREADS) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void stream_bf16_kernel(FfnProblem p) {
   __shared__ __attribute__((aligned(16))) char sx[C::NB][C::LDS];
-  stream_tile<C, kUp, kComb>(p, sx);
+  __shared__ __attribute__((aligned(16))) Slot slots[kComb ? C::BM * kRegSlots : 1];
+  stream_tile<C, kUp, kComb>(p, sx, slots);
 }
 
 // ---------------------------------------------------------------------------
@@ -1040,9 +1057,12 @@ template <bool kComb>
 __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
   constexpr int LD = kDnBN8 + 8;                    // LDS row of the combine tile (elements)
   __shared__ __attribute__((aligned(16))) uint16_t s_tile[kComb ? 16 * LD : 1];
+  __shared__ __attribute__((aligned(16))) Slot slots[kComb ? 16 * kRegSlots : 1];
   TileInfo ti;
   const int32_t* sched = p.sched + (kComb ? 2 : 1) * (p.E + 2);
   if (!find_tile(sched, p.offsets, p.E, p.ntok, 16, ti)) return;
+  SlotLoad sl;                                      // the tokens' routing, loaded under the K loop
+  if constexpr (kComb) slots_issue(p.comb, ti.m0, ti.mrows, sl);
   const bool shared = ti.g == p.E;
   const int K = shared ? p.inter_s : p.inter, KB = K / 128;
   const int N = p.dim;
@@ -1106,8 +1126,9 @@ __global__ __launch_bounds__(256) void down_skinny_fp8_kernel(FfnProblem p) {
         for (int i = 0; i < 4; ++i)
           s_tile[r * LD + wave * 16 * kDnNT8 + 16 * j + 4 * grp + i] = f32_to_bf16(acc[j][i]);
     }
+    slots_store(p.comb, ti.mrows, sl, slots);
     __syncthreads();
-    combine_from_lds<uint16_t>(p, s_tile, LD, ti, ti.nt * kDnBN8, kDnBN8);
+    combine_from_lds<uint16_t, 2>(p, slots, s_tile, LD, ti, ti.nt * kDnBN8, kDnBN8);
     return;
   }
   if (r < ti.mrows) {
