@@ -62,8 +62,9 @@ def parse():
 def up_kernel_name(cfg):
     """Name of the up-projection kernel the library launches for cfg (the
     library's rule, on R = T * topk routed rows: 256-token bf16 stream tiles
-    once experts average >= 384 rows, 192-token ones from 64 rows, 128-token
-    ones from 32, 64-token ones from 8, 16-token skinny tiles below; fp8
+    once experts average >= 384 rows, 128-token x 512-row ones from 64 rows,
+    128-token x 256-row ones from 32, 64-token ones from 8, 16-token skinny
+    tiles below; fp8
     192-token stream tiles from 12 rows; bf16 tiles need widths that are
     multiples of 64)."""
     R, E = cfg.T * cfg.topk, cfg.E
@@ -73,7 +74,7 @@ def up_kernel_name(cfg):
         if R >= 384 * E:
             return "moe::stream_bf16_kernel<256-token tiles, up>"
         if R >= 64 * E:
-            return "moe::stream_bf16_kernel<192-token tiles, up>"
+            return "moe::stream_bf16_kernel<128-token x 512-row tiles, up>"
         if R >= 32 * E:
             return "moe::stream_bf16_kernel<128-token tiles, up>"
         if R >= 8 * E:

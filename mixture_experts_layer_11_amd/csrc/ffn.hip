@@ -31,22 +31,21 @@ namespace moe {
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(const int32_t* __restrict__ offsets,
                                                             int E, int ntok, int routed,
                                                             int shared_up, int shared_down,
-                                                            int bm, int nt_up, int nt_up_s,
-                                                            int nt_dn, int bm_s, int e_begin,
+                                                            int bm, int bm_dn, int nt_up, int nt_up_s,
+                                                            int nt_dn, int bm_s, int nt_dn_s, int e_begin,
                                                             int e_end,
                                                             int32_t* __restrict__ sched) {
   __shared__ int sc[3][1024];
   const int g = threadIdx.x;
   int c[3] = {0, 0, 0};
   if (routed && g < E && g >= e_begin && g < e_end) {   // experts outside the range get no tiles
-    const int mt = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
-    c[0] = mt * nt_up;
-    c[1] = mt * nt_dn;
+    const int M = offsets[g + 1] - offsets[g];
+    c[0] = (M + bm - 1) / bm * nt_up;
+    c[1] = (M + bm_dn - 1) / bm_dn * nt_dn;
   } else if (g == E) {
-    const int mt = (ntok + bm - 1) / bm;
-    c[0] = shared_up ? mt * nt_up_s : 0;
-    c[1] = shared_down == 1 ? mt * nt_dn : 0;
-    c[2] = shared_down == 2 ? (ntok + bm_s - 1) / bm_s * nt_dn : 0;
+    c[0] = shared_up ? (ntok + bm - 1) / bm * nt_up_s : 0;
+    c[1] = shared_down == 1 ? (ntok + bm_dn - 1) / bm_dn * nt_dn : 0;
+    c[2] = shared_down == 2 ? (ntok + bm_s - 1) / bm_s * nt_dn_s : 0;
   }
 #pragma unroll
   for (int s = 0; s < 3; ++s) sc[s][g] = c[s];
@@ -311,20 +310,22 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 }
 
 // ---------------------------------------------------------------------------
-// Stream tiles (prefill): 64 to 256 token rows x 256 weight rows per
+// Stream tiles (prefill): 64 to 256 token rows x 256 or 512 weight rows per
 // workgroup of 8 waves (two per SIMD), on v_mfma_f32_32x32x16_bf16 (the
 // 32x32 shape runs at full rate on gfx950; 16x16x32 issues at half rate).
 // A tile covers a whole expert whenever it has no more rows than the tile,
 // so each weight slice is fetched from HBM once per expert.
-//   A operand = 32 weight rows per wave, loaded straight from global memory
-//     through a ring of 4 register stages (three 64-element K slices in
-//     flight); for the up projection rows 0-15 are W1 rows and rows 16-31 the
-//     same rows of W3, so a lane's result elements i and i+8 are the two
-//     branches of one h column and SwiGLU needs no data exchange.
-//   B operand = token rows, staged in LDS (four buffers, one workgroup
-//     barrier per two slices) and read by all 8 waves: the slice of every
+//   A operand = one or two 32-row weight tiles per wave, loaded straight from
+//     global memory through a ring of register stages (two or three K slices
+//     of 32 or 64 elements in flight); for the up projection rows 0-15 of a
+//     tile are W1 rows and rows 16-31 the same rows of W3, so a lane's result
+//     elements i and i+8 are the two branches of one h column and SwiGLU
+//     needs no data exchange.
+//   B operand = token rows, staged in LDS (four or eight buffers, one
+//     workgroup barrier per half of them) and read by all 8 waves (each token
+//     fragment feeds the wave's one or two A tiles): the slice of every
 //     n-tile of an expert is the same, so it is mostly L2-resident.
-// Loaded HBM latency is several microseconds, so weights run three 64-element
+// Loaded HBM latency is several microseconds, so weights run several K
 // slices ahead and token slices are loaded into registers a few steps before
 // their LDS store.
 // Memory counters retire in issue order; each step issues its token slice
@@ -333,17 +334,19 @@ __global__ __launch_bounds__(256) void down_skinny_kernel(FfnProblem p) {
 // number of 32-row token sub-tiles it computes.  LDS rows are padded by 16
 // bytes so the fragment reads of a wave spread over the banks.
 // ---------------------------------------------------------------------------
-// Tile shape of the stream kernel: BM token rows, WAVES waves of 32 weight
-// rows each, 64-element K slices.
-template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4, int WPE_ = 2, bool NTW_ = false>
+// Tile shape of the stream kernel: BM token rows, WAVES waves of NA 32-row
+// weight tiles each, BK-element K slices.
+template <int BM_, int WAVES_, int RING_, int XD_ = 2, int NB_ = 4, int WPE_ = 2, bool NTW_ = false,
+          int NA_ = 1, int BK_ = 64>
 struct SCfg {
   static constexpr int BM = BM_;
   static constexpr int WAVES = WAVES_;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int MT = BM / 32;               // 32-row token sub-tiles
-  static constexpr int BN = WAVES * 32;            // weight rows per tile
+  static constexpr int NA = NA_;                   // 32-row weight tiles per wave
+  static constexpr int BN = WAVES * 32 * NA;       // weight rows per tile
   static constexpr int UPBN = BN / 2;              // h columns per up tile
-  static constexpr int BK = 64;                    // K elements per step
+  static constexpr int BK = BK_;                   // K elements per step (32 or 64)
   static constexpr int KS = BK / 16;               // MFMA k-steps per step
   static constexpr int STRIDE = 2 * BK + 16;       // LDS bytes per token row
   static constexpr int LDS = BM * STRIDE;
@@ -357,9 +360,19 @@ struct SCfg {
   static constexpr int UNROLL = std::lcm(std::lcm(RING, XD), D);   // steps with compile-time stage indices
   static constexpr int WPE = WPE_;                 // waves per SIMD (workgroups per CU * WAVES / 4)
   static constexpr bool NTW = NTW_;                // weights through non-temporal loads
-  static_assert(NB == 2 || NB == 4, "two or four token buffers");
+  static_assert(NB == 2 || NB == 4 || NB == 8, "two, four or eight token buffers");
 };
-using SBig = SCfg<192, 8, 4, 3>;  // whole experts of ~128-192 tokens, one workgroup per CU
+// whole experts of ~128-192 tokens (down projection), one workgroup per CU
+using SBig = SCfg<192, 8, 4, 3>;
+// The up projection of the same batches: 128 tokens x 512 weight rows, two
+// 32-row A tiles per wave sharing each token fragment, 32-element K steps so
+// a 4-stage weight ring fits beside the doubled accumulators, 8 token
+// buffers (a barrier every 4 steps).  Half the n-tiles of 256-row tiles, so
+// half the token re-reads through L2 and half the LDS fragment reads per
+// MFMA (up launch of the DeepSeek-V3 layer at 4096 tokens 3.37 -> 3.20 ms;
+// on the down projection the same tiles were slower, and 192-token or
+// 64-element-step versions with deeper rings need scratch)
+using SBigUp = SCfg<128, 8, 4, 2, 8, 2, false, 2, 32>;
 using SHuge = SCfg<256, 8, 2, 1>; // experts of many hundred tokens: larger tiles, shallower rings
 // 64-token tiles of 256 weight rows (8 waves); used while experts average
 // fewer than 32 rows, so their weights are always read non-temporally
@@ -378,7 +391,7 @@ using SComb = SCfg<MOE_COMB_BM, 8, 4, (MOE_COMB_BM >= 128 ? 3 : 2), 4, 2, false>
 template <class C>
 struct StreamSrc {
   const char* x[C::XLOADS];  // token rows (tid / TPR) + ROWS_PER_PASS*i, at byte 16*(tid % TPR)
-  const char* w;             // this lane's weight row, at byte 16*(lane/32)
+  const char* w[C::NA];      // this lane's row of each weight tile, at byte 16*(lane/32)
   int lds_st;                // LDS byte offset of this thread's token chunk
   bool xact[C::XLOADS];      // row inside the tile (for BM not a multiple of the pass)
 };
@@ -390,19 +403,21 @@ __device__ __forceinline__ f32x16_t mma32(f32x16_t c, uint4 a, uint4 b) {
 
 template <class C, int MT>
 __device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const StreamSrc<C>& S, int nk,
-                                             f32x16_t (&acc)[C::MT]) {
+                                             f32x16_t (&acc)[C::NA][C::MT]) {
   const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
-  uint4 wr[C::RING][C::KS];   // weight slices in flight: [slice % RING][k-step]
+  uint4 wr[C::RING][C::NA][C::KS];   // weight slices in flight: [slice % RING][tile][k-step]
   // token load passes that reach the MT*32 rows this instantiation reads
   constexpr int XL = std::min(C::XLOADS, (32 * MT + C::ROWS_PER_PASS - 1) / C::ROWS_PER_PASS);
   uint4 xr[C::XD][C::XLOADS]; // token slices in flight between load and LDS store: [slice % XD]
-  auto wload = [&](uint4 (&dst)[C::KS], int kt) {
+  auto wload = [&](uint4 (&dst)[C::NA][C::KS], int kt) {
     kt = kt < nk ? kt : nk - 1;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {   // k-step s: bytes 32s + 16*(lane/32) of the 128-byte slice
-      const char* a = S.w + kt * (2 * kChunkStride) + (s >> 1) * kChunkStride + (s & 1) * 512;
-      dst[s] = C::NTW ? ldg16_stream(a) : ldg16(a);
-    }
+    for (int j = 0; j < C::NA; ++j)
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {   // k-step s: bytes 32s + 16*(lane/32) of the 2*BK-byte slice
+        const char* a = S.w[j] + ((kt * 2 * C::BK + 32 * s) >> 6) * kChunkStride + (s & 1) * 512;
+        dst[j][s] = C::NTW ? ldg16_stream(a) : ldg16(a);
+      }
   };
   auto xload = [&](uint4 (&dst)[C::XLOADS], int kt) {
     kt = kt < nk ? kt : nk - 1;
@@ -451,9 +466,10 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const St
       for (int a = 0; a < MT; ++a) {
         if (s + 1 < C::KS)
           fx[(s + 1) & 1][a] = *reinterpret_cast<const uint4*>(sb + 32 * a * C::STRIDE + 32 * (s + 1));
-        acc[a] = mma32(acc[a], wr[ws][s], fx[s & 1][a]);
+#pragma unroll
+        for (int j = 0; j < C::NA; ++j) acc[j][a] = mma32(acc[j][a], wr[ws][j][s], fx[s & 1][a]);
         if (s + 1 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, C::NA, 0);   // MFMA
       }
     }
     xstore(xr[(r + C::D) % C::XD], (kt + C::D) % C::NB);
@@ -513,36 +529,43 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
   S.lds_st = lr * C::STRIDE + 16 * lc;
 
   const int fr = lane & 31, fg = lane >> 5;
-  int ncol0;                        // first output column of the wave
-  bool wave_active;
-  if (kUp) {
-    // A rows 0-15: W1 rows ncol0 + [0,16); rows 16-31: the same rows of W3
-    ncol0 = ti.nt * C::UPBN + wave * 16;
-    wave_active = ncol0 < N;
-    const int n = min(ncol0 + (fr & 15), N - 1);
-    const uint16_t* W = fr < 16 ? (shared ? static_cast<const uint16_t*>(p.ws1)
-                                          : static_cast<const uint16_t*>(p.w1) + (size_t)(ti.g - p.e_begin) * N * K)
-                                : (shared ? static_cast<const uint16_t*>(p.ws3)
-                                          : static_cast<const uint16_t*>(p.w3) + (size_t)(ti.g - p.e_begin) * N * K);
-    S.w = reinterpret_cast<const char*>(W) + wtile_off(n, 16 * fg, 2 * K);
-  } else {
-    ncol0 = ti.nt * C::BN + wave * 32;
-    wave_active = ncol0 < N;
-    const uint16_t* W2 = shared ? static_cast<const uint16_t*>(p.ws2)
-                                : static_cast<const uint16_t*>(p.w2) + (size_t)(ti.g - p.e_begin) * N * K;
-    S.w = reinterpret_cast<const char*>(W2) + wtile_off(min(ncol0 + fr, N - 1), 16 * fg, 2 * K);
+  // weight tile j of the wave: up - h columns ncol[j] + [0,16), A rows 0-15
+  // from W1 and 16-31 the same rows of W3; down - output columns ncol[j] + [0,32)
+  int ncol[C::NA];
+  bool tile_active[C::NA];
+  bool wave_active = false;
+#pragma unroll
+  for (int j = 0; j < C::NA; ++j) {
+    if (kUp) {
+      ncol[j] = ti.nt * C::UPBN + (wave * C::NA + j) * 16;
+      const int n = min(ncol[j] + (fr & 15), N - 1);
+      const uint16_t* W = fr < 16 ? (shared ? static_cast<const uint16_t*>(p.ws1)
+                                            : static_cast<const uint16_t*>(p.w1) + (size_t)(ti.g - p.e_begin) * N * K)
+                                  : (shared ? static_cast<const uint16_t*>(p.ws3)
+                                            : static_cast<const uint16_t*>(p.w3) + (size_t)(ti.g - p.e_begin) * N * K);
+      S.w[j] = reinterpret_cast<const char*>(W) + wtile_off(n, 16 * fg, 2 * K);
+    } else {
+      ncol[j] = ti.nt * C::BN + (wave * C::NA + j) * 32;
+      const uint16_t* W2 = shared ? static_cast<const uint16_t*>(p.ws2)
+                                  : static_cast<const uint16_t*>(p.w2) + (size_t)(ti.g - p.e_begin) * N * K;
+      S.w[j] = reinterpret_cast<const char*>(W2) + wtile_off(min(ncol[j] + fr, N - 1), 16 * fg, 2 * K);
+    }
+    tile_active[j] = ncol[j] < N;
+    wave_active = wave_active || tile_active[j];
   }
   // every wave runs the same instantiation: the token slices are loaded by
-  // all threads of the workgroup (a wave past the last column computes on a
-  // clamped weight row and stores nothing)
+  // all threads of the workgroup (a weight tile past the last column computes
+  // on a clamped weight row and stores nothing)
   int m_active = (rows_left + 31) >> 5;
   m_active = m_active > C::MT ? C::MT : m_active;
 
-  f32x16_t acc[C::MT];
+  f32x16_t acc[C::NA][C::MT];
 #pragma unroll
-  for (int a = 0; a < C::MT; ++a)
+  for (int j = 0; j < C::NA; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[a][i] = 0.f;
+    for (int a = 0; a < C::MT; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][a][i] = 0.f;
 
   const int nk = K / C::BK;
   // the K loop is instantiated for every sub-tile count, so no MFMA or token
@@ -555,8 +578,10 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
     uint16_t* st = reinterpret_cast<uint16_t*>(&sx[0][0]);
     slots_store(p.comb, rows_left, sl, slots);
     __syncthreads();                  // every wave is done with the token buffers
-    if (wave_active) {
-      const int ml = lane & 31, rg = 4 * (lane >> 5);
+    const int ml = lane & 31, rg = 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < C::NA; ++j) {
+      if (!tile_active[j]) continue;
 #pragma unroll
       for (int a = 0; a < C::MT; ++a) {
         const int r = 32 * a + ml;
@@ -564,9 +589,9 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           uint2 o;
-          o.x = (uint32_t)f32_to_bf16(acc[a][4 * q]) | ((uint32_t)f32_to_bf16(acc[a][4 * q + 1]) << 16);
-          o.y = (uint32_t)f32_to_bf16(acc[a][4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[a][4 * q + 3]) << 16);
-          *reinterpret_cast<uint2*>(st + r * LD + wave * 32 + 8 * q + rg) = o;
+          o.x = (uint32_t)f32_to_bf16(acc[j][a][4 * q]) | ((uint32_t)f32_to_bf16(acc[j][a][4 * q + 1]) << 16);
+          o.y = (uint32_t)f32_to_bf16(acc[j][a][4 * q + 2]) | ((uint32_t)f32_to_bf16(acc[j][a][4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(st + r * LD + (wave * C::NA + j) * 32 + 8 * q + rg) = o;
         }
       }
     }
@@ -577,29 +602,33 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
   if (!wave_active) return;
 
   // epilogue: lane holds D[row = 8*(i/4) + 4*(lane/32) + i%4][col = lane % 32]
-  // (row = weight row of the wave, col = token of the sub-tile)
+  // (row = weight row of the tile, col = token of the sub-tile)
   const int ml = lane & 31, rg = 4 * (lane >> 5);
 #pragma unroll
-  for (int a = 0; a < C::MT; ++a) {
-    const int m = m0 + 32 * a + ml;
-    if (a >= m_active || m >= m0 + rows_left) continue;
-    if (kUp) {
-      uint16_t* hrow = shared ? static_cast<uint16_t*>(p.hs) + (size_t)m * N
-                              : static_cast<uint16_t*>(p.h) + (size_t)(ti.row0 + m) * N;
+  for (int j = 0; j < C::NA; ++j) {
+    if (!tile_active[j]) continue;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {       // rows 8q + rg + [0,4) of W1, 16 + same of W3
-        float v[4];
+    for (int a = 0; a < C::MT; ++a) {
+      const int m = m0 + 32 * a + ml;
+      if (a >= m_active || m >= m0 + rows_left) continue;
+      if (kUp) {
+        uint16_t* hrow = shared ? static_cast<uint16_t*>(p.hs) + (size_t)m * N
+                                : static_cast<uint16_t*>(p.h) + (size_t)(ti.row0 + m) * N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = silu(acc[a][4 * q + i]) * acc[a][8 + 4 * q + i];
-        store4<uint16_t>(hrow + ncol0 + 8 * q + rg, v);
-      }
-    } else {
-      uint16_t* orow = shared ? static_cast<uint16_t*>(p.shared_out) + (size_t)m * N
-                              : static_cast<uint16_t*>(p.out) + (size_t)(ti.row0 + m) * N;
+        for (int q = 0; q < 2; ++q) {       // rows 8q + rg + [0,4) of W1, 16 + same of W3
+          float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4] = {acc[a][4 * q], acc[a][4 * q + 1], acc[a][4 * q + 2], acc[a][4 * q + 3]};
-        store4<uint16_t>(orow + ncol0 + 8 * q + rg, v);
+          for (int i = 0; i < 4; ++i) v[i] = silu(acc[j][a][4 * q + i]) * acc[j][a][8 + 4 * q + i];
+          store4<uint16_t>(hrow + ncol[j] + 8 * q + rg, v);
+        }
+      } else {
+        uint16_t* orow = shared ? static_cast<uint16_t*>(p.shared_out) + (size_t)m * N
+                                : static_cast<uint16_t*>(p.out) + (size_t)(ti.row0 + m) * N;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4] = {acc[j][a][4 * q], acc[j][a][4 * q + 1], acc[j][a][4 * q + 2], acc[j][a][4 * q + 3]};
+          store4<uint16_t>(orow + ncol[j] + 8 * q + rg, v);
+        }
       }
     }
   }
@@ -1163,7 +1192,8 @@ enum class Tiles { Skinny, Mid, Big, Huge };
 // below 8 rows (decode: weight streaming, each expert's weights read once);
 // from there every 16-token m-tile would re-read its expert's weights, so
 // stream tiles take over - 64-token tiles below 32 rows, 128-token tiles
-// below 64, whole-expert 192-token tiles up to 384 rows, 256-token tiles above
+// below 64, whole-expert tiles up to 384 rows (128 x 512 up tiles, 192 x 256
+// down tiles), 256-token tiles above
 // (hot experts of many hundred rows).  fp8 weights switch to their 192-token
 // stream tiles from 12 rows.  Stream tiles need widths that are multiples of 64.
 static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
@@ -1182,6 +1212,8 @@ struct FfnPlan {
   Tiles t;
   bool nt;              // stream tiles read their weights non-temporally
   int bm, nt_up, nt_up_s, nt_dn, threads;
+  int bm_dn, threads_dn;   // tile rows and threads of the down launch
+  int nt_dn_s;          // n-tiles of the shared down + combine launch
   int bm_s, threads_s;       // tile rows and threads of the shared down + combine launch
   long g_up, g_dn, g_dn_s;   // workgroups (multiples of 8): up, down, shared down + combine
 };
@@ -1203,8 +1235,10 @@ static FfnPlan plan_ffn(const FfnProblem& p) {
   if (L.t == Tiles::Big && f8) L.bm = F8::BM, bn_up = F8::UPBN, bn_dn = F8::BN, L.threads = F8::THREADS;
   else if (L.t == Tiles::Huge) L.bm = SHuge::BM, bn_up = SHuge::UPBN, bn_dn = SHuge::BN, L.threads = SHuge::THREADS;
   else if (L.t == Tiles::Big && L.nt) L.bm = SBigNT::BM, bn_up = SBigNT::UPBN, bn_dn = SBigNT::BN, L.threads = SBigNT::THREADS;
-  else if (L.t == Tiles::Big) L.bm = SBig::BM, bn_up = SBig::UPBN, bn_dn = SBig::BN, L.threads = SBig::THREADS;
+  else if (L.t == Tiles::Big) L.bm = SBigUp::BM, bn_up = SBigUp::UPBN, bn_dn = SBig::BN, L.threads = SBigUp::THREADS;
   else if (L.t == Tiles::Mid) L.bm = SMid::BM, bn_up = SMid::UPBN, bn_dn = SMid::BN, L.threads = SMid::THREADS;
+  L.bm_dn = L.bm, L.threads_dn = L.threads;
+  if (L.t == Tiles::Big && !f8 && !L.nt) L.bm_dn = SBig::BM, L.threads_dn = SBig::THREADS;
   L.nt_up = ceil_div(p.inter, bn_up);
   L.nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
   L.nt_dn = ceil_div(p.dim, bn_dn);
@@ -1212,18 +1246,19 @@ static FfnPlan plan_ffn(const FfnProblem& p) {
   const bool comb_cfg = !f8 && L.t != Tiles::Skinny;
   L.bm_s = comb_cfg ? SComb::BM : L.bm;
   L.threads_s = comb_cfg ? SComb::THREADS : L.threads;
+  L.nt_dn_s = comb_cfg ? ceil_div(p.dim, SComb::BN) : L.nt_dn;
   const long Rr = p.routed ? R : 0;
   L.g_up = Rr || p.shared_up ? round8(max_tiles(Rr, p.E, p.ntok, p.shared_up, L.bm, L.nt_up, L.nt_up_s)) : 0;
   const bool dn_store = p.shared_down == SharedDown::Store;
-  L.g_dn = Rr || dn_store ? round8(max_tiles(Rr, p.E, p.ntok, dn_store, L.bm, L.nt_dn, L.nt_dn)) : 0;
-  L.g_dn_s = p.shared_down == SharedDown::Combine ? round8((long)ceil_div(p.ntok, L.bm_s) * L.nt_dn) : 0;
+  L.g_dn = Rr || dn_store ? round8(max_tiles(Rr, p.E, p.ntok, dn_store, L.bm_dn, L.nt_dn, L.nt_dn)) : 0;
+  L.g_dn_s = p.shared_down == SharedDown::Combine ? round8((long)ceil_div(p.ntok, L.bm_s) * L.nt_dn_s) : 0;
   return L;
 }
 
 static long quant_blocks(int ntok, int dim) { return ((long)ntok * (dim / 128) * 16 + 255) / 256; }
 
 static long plan_items(const FfnProblem& p, const FfnPlan& L) {
-  long items = std::max(std::max(L.g_up, L.g_dn) * L.threads, L.g_dn_s * L.threads_s);
+  long items = std::max(std::max(L.g_up * L.threads, L.g_dn * L.threads_dn), L.g_dn_s * L.threads_s);
   if (p.wkind == WKind::FP8) items = std::max(items, quant_blocks(p.ntok, p.dim) * 256);
   return items;
 }
@@ -1266,8 +1301,8 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   const bool f8 = p.wkind == WKind::FP8, nt = L.nt;
   ffn_schedule_kernel<<<1, 1024, 0, st>>>(p.routed ? p.offsets : nullptr, p.E, p.ntok,
                                           p.routed ? 1 : 0, p.shared_up ? 1 : 0,
-                                          (int)p.shared_down, L.bm, L.nt_up, L.nt_up_s, L.nt_dn,
-                                          L.bm_s, p.e_begin, p.e_end, p.sched);
+                                          (int)p.shared_down, L.bm, L.bm_dn, L.nt_up, L.nt_up_s, L.nt_dn,
+                                          L.bm_s, L.nt_dn_s, p.e_begin, p.e_end, p.sched);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const FfnProblem& q = p;
@@ -1285,7 +1320,7 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t st) {
   else if (t == Tiles::Big && f8) stream_fp8_kernel<true, false><<<g_up, F8::THREADS, 0, st>>>(q);
   else if (t == Tiles::Huge) stream_bf16_kernel<SHuge, true><<<g_up, SHuge::THREADS, 0, st>>>(q);
   else if (t == Tiles::Big && nt) stream_bf16_kernel<SBigNT, true><<<g_up, SBigNT::THREADS, 0, st>>>(q);
-  else if (t == Tiles::Big) stream_bf16_kernel<SBig, true><<<g_up, SBig::THREADS, 0, st>>>(q);
+  else if (t == Tiles::Big) stream_bf16_kernel<SBigUp, true><<<g_up, SBigUp::THREADS, 0, st>>>(q);
   else if (t == Tiles::Mid) stream_bf16_kernel<SMid, true><<<g_up, SMid::THREADS, 0, st>>>(q);
   else if (p.wkind == WKind::FP8) up_skinny_fp8_kernel<<<g_up, 256, 0, st>>>(q);
   else if (p.wkind == WKind::BF16) up_skinny_kernel<uint16_t><<<g_up, 256, 0, st>>>(q);

@@ -233,14 +233,16 @@ def test_expert_ffn_parity(cfg, layers):
 
 # Hand-made dispatches whose expert sizes straddle the m-tile boundaries of
 # each tile kind (the average rows per expert R / E picks the kind: 16-token
-# tiles below 8, 64-token tiles below 32, 128-token tiles below 64, 192-token
-# tiles below 384, 256-token tiles above; fp8 192-token tiles from 12,
-# 16-token fp8 tiles below).  An
+# tiles below 8, 64-token tiles below 32, 128-token tiles below 64, then
+# 128-token x 512-row up tiles with 192-token down tiles below 384, 256-token
+# tiles above; fp8 192-token tiles from 12, 16-token fp8 tiles below).  An
 # expert of M rows runs as ceil(M / BM) m-tiles of equal size, the last
-# taking the rest.
+# taking the rest.  big_bf16_up straddles the 128-row up m-tiles and leaves
+# the second 256-column up n-tile a quarter full (inter 320).
 TILE_CASES = [
     ("mid_bf16", dict(E=8, topk=2, w_dtype="bf16"), [65, 64, 63, 29, 0, 1, 0, 0]),
     ("big_bf16", dict(E=4, topk=2, w_dtype="bf16"), [193, 0, 385, 622]),
+    ("big_bf16_up", dict(E=4, topk=2, w_dtype="bf16", inter=320), [129, 256, 257, 128]),
     ("big_nt_bf16", dict(E=8, topk=2, w_dtype="bf16"), [129, 128, 1, 0, 65, 33, 27, 1]),
     ("huge_bf16", dict(E=4, topk=2, w_dtype="bf16"), [257, 513, 1, 829]),
     ("skinny_bf16", dict(E=8, topk=2, w_dtype="bf16"), [17, 0, 16, 15, 1, 1, 2, 0]),
@@ -249,9 +251,10 @@ TILE_CASES = [
 ]
 
 
-# the shortest K loops: one or two steps per tile (64-wide bf16, 128-wide fp8)
+# the shortest K loops: one to four steps per tile (32- or 64-wide bf16, 128-wide fp8)
 SHORT_K_CASES = [
     ("big_bf16_k64", dict(E=4, topk=2, w_dtype="bf16", dim=64, inter=64, inter_shared=64), [193, 0, 385, 622]),
+    ("big_bf16_up_k64", dict(E=4, topk=2, w_dtype="bf16", dim=64, inter=64, inter_shared=64), [129, 256, 257, 128]),
     ("huge_bf16_k128", dict(E=4, topk=2, w_dtype="bf16", dim=128, inter=64, inter_shared=128), [257, 513, 1, 829]),
     ("mid_bf16_k64", dict(E=8, topk=2, w_dtype="bf16", dim=64, inter=128, inter_shared=64), [65, 64, 63, 29, 0, 1, 0, 0]),
     ("big_fp8_k128", dict(E=4, topk=2, w_dtype="fp8", dim=128, inter=128, inter_shared=128), [193, 385, 1, 21]),
