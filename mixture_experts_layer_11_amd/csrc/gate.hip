@@ -204,13 +204,15 @@ __global__ __launch_bounds__(256, 2) void router_mfma_kernel(const uint16_t* __r
 //   topk rounds of a wave arg-max over the candidates, ordered by
 //   (s' descending, expert id ascending); the winner's unbiased s is its weight
 //   sigmoid: w /= sum(w); then w *= route_scale
-// Lane l holds experts l, l+64, ... (up to 8 per lane, E <= 512).
+// Lane l holds experts l, l+64, ... (PL = ceil(E/64) per lane, E <= 512).
 // ---------------------------------------------------------------------------
 constexpr int kSelWaves = 4;
-constexpr int kMaxPerLane = 8;
 
 // `logits` holds `splits` partial logit arrays of ntok*E values each (one when
-// the router did not split K); they are summed in split order, in fp32.
+// the router did not split K); they are summed in split order, in fp32.  The
+// loads of up to 16 splits are in flight at once (all of them: the router
+// splits K at most 16 ways), then summed in split order.
+template <int PL>
 __global__ __launch_bounds__(256) void gate_select_kernel(
     const float* __restrict__ logits, int splits, const float* __restrict__ bias, int ntok, int E,
     int n_groups, int topk_groups, int topk, int score_softmax, float route_scale,
@@ -223,22 +225,24 @@ __global__ __launch_bounds__(256) void gate_select_kernel(
   const bool active = t < ntok;
   const int tt = active ? t : ntok - 1;
 
+  constexpr int kMaxPerLane = PL;
+  constexpr int QR = 64 / PL < 16 ? 64 / PL : 16;   // splits whose loads are in flight together
   float s[kMaxPerLane], sp[kMaxPerLane];
   const float* zrow = logits + (size_t)tt * E;
   const size_t stride = (size_t)ntok * E;
 #pragma unroll
   for (int j = 0; j < kMaxPerLane; ++j) s[j] = lane + 64 * j < E ? zrow[lane + 64 * j] : 0.f;
-  for (int q0 = 1; q0 < splits; q0 += 4) {   // 4 splits' loads in flight, summed in split order
-    float v[4][kMaxPerLane];
+  for (int q0 = 1; q0 < splits; q0 += QR) {  // summed in split order
+    float v[QR][kMaxPerLane];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
+    for (int qq = 0; qq < QR; ++qq)
 #pragma unroll
       for (int j = 0; j < kMaxPerLane; ++j) {
         const int e = lane + 64 * j;
         v[qq][j] = (q0 + qq < splits && e < E) ? zrow[(size_t)(q0 + qq) * stride + e] : 0.f;
       }
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
+    for (int qq = 0; qq < QR; ++qq)
 #pragma unroll
       for (int j = 0; j < kMaxPerLane; ++j) s[j] += v[qq][j];
   }
@@ -343,6 +347,21 @@ __global__ __launch_bounds__(256) void gate_select_kernel(
   }
 }
 
+// gate_select_kernel<PL> with PL = ceil(E / 64) rounded up to a power of two
+static void launch_select(const float* logits, int splits, const float* bias, int ntok, int E,
+                          int n_groups, int topk_groups, int topk, int softmax, float route_scale,
+                          int32_t* topk_idx, float* topk_w, hipStream_t st) {
+  const int g = (ntok + kSelWaves - 1) / kSelWaves;
+  if (E <= 64)
+    gate_select_kernel<1><<<g, 256, 0, st>>>(logits, splits, bias, ntok, E, n_groups, topk_groups, topk, softmax, route_scale, topk_idx, topk_w);
+  else if (E <= 128)
+    gate_select_kernel<2><<<g, 256, 0, st>>>(logits, splits, bias, ntok, E, n_groups, topk_groups, topk, softmax, route_scale, topk_idx, topk_w);
+  else if (E <= 256)
+    gate_select_kernel<4><<<g, 256, 0, st>>>(logits, splits, bias, ntok, E, n_groups, topk_groups, topk, softmax, route_scale, topk_idx, topk_w);
+  else
+    gate_select_kernel<8><<<g, 256, 0, st>>>(logits, splits, bias, ntok, E, n_groups, topk_groups, topk, softmax, route_scale, topk_idx, topk_w);
+}
+
 hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bias, int ntok,
                        int dim, int E, int n_groups, int topk_groups, int topk, bool softmax,
                        float route_scale, float* logits, float* rpart, int32_t* topk_idx,
@@ -361,17 +380,15 @@ hipError_t launch_gate(const void* x, const void* wr, bool f32, const float* bia
     if (S > 1) {   // the selection sums the split partials as it reads them
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      gate_select_kernel<<<(ntok + kSelWaves - 1) / kSelWaves, 256, 0, st>>>(
-          rpart, S, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0, route_scale,
-          topk_idx, topk_w);
+      launch_select(rpart, S, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0,
+                    route_scale, topk_idx, topk_w, st);
       return hipGetLastError();
     }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  gate_select_kernel<<<(ntok + kSelWaves - 1) / kSelWaves, 256, 0, st>>>(
-      logits, 1, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0, route_scale,
-      topk_idx, topk_w);
+  launch_select(logits, 1, bias, ntok, E, n_groups, topk_groups, topk, softmax ? 1 : 0,
+                route_scale, topk_idx, topk_w, st);
   return hipGetLastError();
 }
 
