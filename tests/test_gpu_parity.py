@@ -73,6 +73,12 @@ GATE_CFGS = ALL_SMALL + inputs.CONFIGS + [
     tiny_cfg("E512_topk1", T=70, E=512, n_groups=8, topk_groups=1, topk=1, dim=128,
              act_dtype="bf16", router_dtype="bf16", w_dtype="bf16"),
     tiny_cfg("T1", T=1, E=16, n_groups=4, topk_groups=2, topk=4),
+    # two experts per lane of the selection wave, the router's K split 16 ways
+    tiny_cfg("E128_split16", T=96, E=128, n_groups=4, topk_groups=2, topk=6, dim=1024,
+             act_dtype="bf16", router_dtype="bf16", w_dtype="bf16"),
+    # an expert count that leaves the selection wave's last slots partly empty
+    tiny_cfg("E200_groups", T=130, E=200, n_groups=8, topk_groups=3, topk=7, dim=512,
+             act_dtype="bf16", router_dtype="bf16", w_dtype="bf16"),
 ]
 
 
