@@ -1211,11 +1211,11 @@ static Tiles pick_tiles(const FfnProblem& p, bool has_shared) {
 struct FfnPlan {
   Tiles t;
   bool nt;              // stream tiles read their weights non-temporally
-  int bm, nt_up, nt_up_s, nt_dn, threads;
-  int bm_dn, threads_dn;   // tile rows and threads of the down launch
-  int nt_dn_s;          // n-tiles of the shared down + combine launch
-  int bm_s, threads_s;       // tile rows and threads of the shared down + combine launch
-  long g_up, g_dn, g_dn_s;   // workgroups (multiples of 8): up, down, shared down + combine
+  int bm, threads;            // tile rows and threads of the up launch
+  int nt_up, nt_up_s;         // its n-tiles per routed expert and for the shared expert
+  int bm_dn, threads_dn, nt_dn;   // the down launch
+  int bm_s, threads_s, nt_dn_s;   // the shared down + combine launch
+  long g_up, g_dn, g_dn_s;    // workgroups (multiples of 8): up, down, shared down + combine
 };
 
 static long round8(long n) { return (n + 7) / 8 * 8; }
@@ -1242,10 +1242,11 @@ static FfnPlan plan_ffn(const FfnProblem& p) {
   L.nt_up = ceil_div(p.inter, bn_up);
   L.nt_up_s = has_shared ? ceil_div(p.inter_s, bn_up) : 0;
   L.nt_dn = ceil_div(p.dim, bn_dn);
-  // the bf16 stream kinds fuse the combine on SComb tiles (same 256 columns)
+  // the bf16 stream kinds fuse the combine on SComb tiles; the others on the
+  // down launch's own tiles
   const bool comb_cfg = !f8 && L.t != Tiles::Skinny;
-  L.bm_s = comb_cfg ? SComb::BM : L.bm;
-  L.threads_s = comb_cfg ? SComb::THREADS : L.threads;
+  L.bm_s = comb_cfg ? SComb::BM : L.bm_dn;
+  L.threads_s = comb_cfg ? SComb::THREADS : L.threads_dn;
   L.nt_dn_s = comb_cfg ? ceil_div(p.dim, SComb::BN) : L.nt_dn;
   const long Rr = p.routed ? R : 0;
   L.g_up = Rr || p.shared_up ? round8(max_tiles(Rr, p.E, p.ntok, p.shared_up, L.bm, L.nt_up, L.nt_up_s)) : 0;
