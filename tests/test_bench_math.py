@@ -100,3 +100,29 @@ def test_floor_takes_the_binding_roof():
     f = bench.floors(cfg, res)
     assert f["binding"] == "hbm" and f["t_floor_ms"] == pytest.approx(2.0)
     assert f["roofline_frac"] == pytest.approx(0.5)
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_measured_on(monkeypatch):
+    """The roofline object's measured HBM traffic comes from profiles/traffic.json
+    and must turn null once the expert-kernel sources hash differently from the
+    hash recorded with the counters."""
+    import json
+    import os
+    path = os.path.join(bench.ROOT, "profiles", "traffic.json")
+    with open(path) as f:
+        rec = json.load(f)
+    key = "up_grouped_gemm@c1_dsv3_decode_T128"
+    assert key in rec, "the decode up launch's traffic record is missing"
+    ent = rec[key]
+    assert ent["hbm_bytes_per_launch"] > 0 and len(ent["source_sha"]) == 16
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: ent["source_sha"])
+    assert bench.traffic_for("up_grouped_gemm", "c1_dsv3_decode_T128") == ent["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 16)
+    assert bench.traffic_for("up_grouped_gemm", "c1_dsv3_decode_T128") is None
+    assert bench.traffic_for("up_grouped_gemm", "no_such_workload") is None
+
+
+def test_kernel_source_hash_covers_every_expert_kernel_source():
+    """The hash behind the traffic record covers the files the expert kernels
+    are compiled from, the combine header included."""
+    assert set(bench.KERNEL_SOURCES) >= {"ffn.hip", "common.h", "kernels.h", "combine.h"}
