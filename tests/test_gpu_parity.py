@@ -183,7 +183,8 @@ def test_gate_exact_ties_go_to_lower_id(kind, act):
 @pytest.mark.parametrize("T,E,K", [(1, 8, 2), (63, 16, 4), (64, 16, 4), (65, 32, 8),
                                    (128, 256, 8), (256, 512, 32), (257, 256, 8),
                                    (1000, 256, 8), (4096, 256, 8), (8192, 64, 6),
-                                   (777, 512, 32), (300, 3, 3)])
+                                   (777, 512, 32), (300, 3, 3),
+                                   (70000, 64, 6)])   # past 2^16 tokens: 274 count blocks
 def test_permute_bitexact(T, E, K):
     rng = np.random.default_rng(T * 1000 + E)
     # skewed draws: half the rows favour a few experts
@@ -630,6 +631,10 @@ EDGE_CFGS = [
     tiny_cfg("edge_hot_all", T=90, E=16, n_groups=1, topk_groups=1, topk=2, score_func="softmax",
              bias_range=None, hot_experts=1, hot_scale=64.0, act_dtype="bf16",
              router_dtype="bf16", w_dtype="bf16"),
+    # past 2^16 tokens: 264,000 routed rows, ~16,500 per expert (256-token
+    # stream tiles, 65 m-tiles per expert), 16,500 selection workgroups
+    tiny_cfg("edge_T66000_bf16", T=66000, E=16, n_groups=4, topk_groups=2, topk=4, dim=128,
+             inter=128, inter_shared=128, act_dtype="bf16", router_dtype="bf16", w_dtype="bf16"),
 ]
 
 
