@@ -579,7 +579,8 @@ def test_forward_parity_layer_accumulator(ci, layers):
     assert same.mean() > 0.97
 
 
-@pytest.mark.parametrize("ci,rng_", [(1, (8, 24)), (0, (0, 4)), (3, (7, 16)), (9, (2, 5))])
+@pytest.mark.parametrize("ci,rng_", [(1, (8, 24)), (0, (0, 4)), (3, (7, 16)), (9, (2, 5)),
+                                     (5, (3, 11))])   # s5: 128 x 512 up tiles
 def test_forward_parity_expert_range(ci, rng_):
     # one rank's share: only experts b..e-1 are uploaded and computed
     cfg = inputs.SMALL_CONFIGS[ci]
