@@ -653,7 +653,7 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
 // epilogue quantises h per 1x128 block: the 8 waves' 16-column slices of a
 // token row form exactly one block, so the amax is reduced across waves in LDS.
 // ---------------------------------------------------------------------------
-using F8 = SCfg<192, 8, 2, 1>;   // 192 tokens, 8 waves x 32 weight rows, ring of 2
+using F8 = SCfg<192, 8, 3, 1>;   // 192 tokens, 8 waves x 32 weight rows, a weight ring of 3
 constexpr int kF8MT = F8::BM / 32;
 
 struct StreamSrcF8 {
@@ -705,60 +705,61 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
       sxs[buf][(threadIdx.x >> 3) + F8::ROWS_PER_PASS * i] = sc[i];   // equal values from the row's 8 lanes
     }
   };
-  // the token staging of the bf16 stream loop: slice j in LDS buffer j % NB,
-  // slice kt+D stored after step kt, one barrier every D steps
+  // Token slice j lives in LDS buffer j % NB; slice kt+D is stored after step
+  // kt, one barrier every D steps (the staging of the bf16 stream loop).
+  // Order of issue: a step issues its weight slice first and its token slice
+  // last, after storing the token slice issued at the end of the step before.
+  // Memory counters retire in issue order, so that store waits only for the
+  // loads issued up to the previous step's end: weight slices stay in flight
+  // for RING-1 = 2 steps and each token slice for one whole step.  (Issued at
+  // the start of the step and stored at its end, the token slice also made
+  // every older weight slice land, whatever the ring depth.)
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     xload(xr[j % XD], xsr[j % XD], j);
     xstore(xr[j % XD], xsr[j % XD], j);
   }
 #pragma unroll
-  for (int j = D; j < D + XD - 1; ++j) xload(xr[j % XD], xsr[j % XD], j);
-#pragma unroll
   for (int j = 0; j < RING - 1; ++j) wload(wr[j], wsc[j], j);
+#pragma unroll
+  for (int j = D; j < D + XD; ++j) xload(xr[j % XD], xsr[j % XD], j);
   __syncthreads();
   auto step = [&](int kt, auto R) {
     constexpr int r = decltype(R)::value;
     constexpr int ws = r % RING;
-    constexpr int xl = (r + D - 1 + XD) % XD;
-    xload(xr[xl], xsr[xl], kt + D - 1 + XD);
     wload(wr[(ws + RING - 1) % RING], wsc[(ws + RING - 1) % RING], kt + RING - 1);
     __builtin_amdgcn_sched_barrier(0);
     const char* sb = sx[kt % NB] + fr * F8::STRIDE + 32 * fg;
     const float* sbs = sxs[kt % NB] + fr;
-    // the fragments and scale of sub-tile a+1 are read from LDS while
-    // sub-tile a is multiplied; the promotion of sub-tile a-1 follows the
-    // MFMAs of sub-tile a, so it never waits for them
-    i32x8_t_ bx[2][2];
-    float xsc[2];
+    // the fragments and scale of sub-tile a are read from LDS just before its
+    // MFMAs (one buffer: the registers went to the weight ring; the other wave
+    // of the SIMD covers the read latency); the promotion of sub-tile a-1
+    // follows the MFMAs of sub-tile a, so it never waits for them
+    i32x8_t_ bx[2];
     f32x16_t part[2];              // partial products of the block, sub-tiles a-1 and a
-    auto frag = [&](int a, int b) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bx[b][j] = *reinterpret_cast<const i32x8_t_*>(sb + 32 * a * F8::STRIDE + 64 * j);
-      xsc[b] = sbs[32 * a];
-    };
     // acc += s * partial with s = w_scale * a_scale, one s per half of D
     auto promote = [&](int a, float as) {
       const float s0 = wsc[ws][0] * as, s1 = wsc[ws][1] * as;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][i] = fmaf(part[a & 1][i], i < 8 ? s0 : s1, acc[a][i]);
     };
-    frag(0, 0);
     float as_prev = 0.f;
 #pragma unroll
     for (int a = 0; a < MT; ++a) {
-      if (a + 1 < MT) frag(a + 1, (a + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bx[j] = *reinterpret_cast<const i32x8_t_*>(sb + 32 * a * F8::STRIDE + 64 * j);
+      const float as = sbs[32 * a];
       __builtin_amdgcn_sched_barrier(0);
-      const float as = xsc[a & 1];
       const f32x16_t zero = {};
-      f32x16_t c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][0], bx[a & 1][0], zero, 0, 0, 0, 127, 0, 127);
-      part[a & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][1], bx[a & 1][1], c, 0, 0, 0, 127, 0, 127);
+      f32x16_t c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][0], bx[0], zero, 0, 0, 0, 127, 0, 127);
+      part[a & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wr[ws][1], bx[1], c, 0, 0, 0, 127, 0, 127);
       if (a > 0) promote(a - 1, as_prev);
       as_prev = as;
       __builtin_amdgcn_sched_barrier(0);
     }
     promote(MT - 1, as_prev);
     xstore(xr[(r + D) % XD], xsr[(r + D) % XD], (kt + D) % NB);
+    xload(xr[(r + D) % XD], xsr[(r + D) % XD], kt + D + XD);
     if (r % D == D - 1) __syncthreads();
   };
   auto body = [&](int kt0, auto... R) { (step(kt0 + decltype(R)::value, R), ...); };
