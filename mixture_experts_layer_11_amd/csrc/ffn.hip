@@ -707,13 +707,12 @@ __device__ __forceinline__ void stream_fp8_kloop(char (&sx)[F8::NB][F8::LDS], fl
   };
   // Token slice j lives in LDS buffer j % NB; slice kt+D is stored after step
   // kt, one barrier every D steps (the staging of the bf16 stream loop).
-  // Order of issue: a step issues its weight slice first and its token slice
-  // last, after storing the token slice issued at the end of the step before.
-  // Memory counters retire in issue order, so that store waits only for the
-  // loads issued up to the previous step's end: weight slices stay in flight
-  // for RING-1 = 2 steps and each token slice for one whole step.  (Issued at
-  // the start of the step and stored at its end, the token slice also made
-  // every older weight slice land, whatever the ring depth.)
+  // Order of issue: a step issues its weight slice first, computes, stores
+  // the token slice issued at the end of the step before and issues the next
+  // one last, ahead of the barrier.  A token slice is thus in flight for a
+  // whole step plus the barrier wait (issued after the barrier, it had only
+  // the step), weight slices for RING-1 = 2 steps; memory counters retire in
+  // issue order, so the store's wait covers only loads issued before it.
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     xload(xr[j % XD], xsr[j % XD], j);
