@@ -317,9 +317,6 @@ def main():
                   "ms_min": round(res["ms_min"], 4), "alg_bytes": int(res["bytes"]),
                   "alg_flops": int(res["flops"]), "down_ms": round(res["down_ms"], 4)},
     }
-    if not a.no_cpu_baseline and not experts:
-        out["cpu_baseline"] = cpu_baseline(layer, a.cpu_tokens)
-    del layer
     extra = {}
     for name in [s for s in a.also.split(",") if s]:
         c2 = inputs.config_by_name(name)
@@ -333,6 +330,11 @@ def main():
         }
     if extra:
         out["also"] = extra
+    # the CPU leg runs after every GPU timing: a GPU left idle for its ~10 s
+    # has shown a first timed launch several milliseconds long
+    if not a.no_cpu_baseline and not experts:
+        out["cpu_baseline"] = cpu_baseline(layer, a.cpu_tokens)
+    del layer
     if peaks:
         out["measured_peaks"] = peaks
     print(json.dumps(out), flush=True)
