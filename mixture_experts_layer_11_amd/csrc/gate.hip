@@ -211,6 +211,42 @@ constexpr int kSelWaves = 4;
 // `logits` holds `splits` partial logit arrays of ntok*E values each (one when
 // the router did not split K); they are summed in split order, in fp32.  The
 // loads of up to 16 splits are in flight at once (all of them: the router
+// One step of the wave arg-max: take the (value, id, score) of the lane that
+// DPP control kCtrl names when it ranks higher - a larger value, or an equal
+// value and a lower id.
+template <int kCtrl>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i, float& s) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, kCtrl, 0xF, 0xF, false);
+  const float os = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), kCtrl, 0xF, 0xF, false));
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; s = os; }
+}
+
+// Arg-max over the wave under that order, result in every lane.  Swaps of
+// lane pairs within quads (quad_perm 1,0,3,2 and 2,3,0,1), then within
+// 8-lane halves (row_half_mirror: k <-> 7-k) and 16-lane rows (row_mirror:
+// k <-> 15-k) leave every lane with its row's best; the four rows' bests are
+// compared in uniform registers.  DPP moves take a few cycles where a
+// shuffle through the LDS crossbar takes a round trip, and the k selection
+// rounds run this back to back.
+__device__ __forceinline__ void wave_argmax(float& v, int& i, float& s) {
+  argmax_dpp_step<0xB1>(v, i, s);
+  argmax_dpp_step<0x4E>(v, i, s);
+  argmax_dpp_step<0x141>(v, i, s);
+  argmax_dpp_step<0x140>(v, i, s);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
+  float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
+#pragma unroll
+  for (int r = 16; r < kWave; r += 16) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r));
+    const int oi = __builtin_amdgcn_readlane(i, r);
+    const float os = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), r));
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; bs = os; }
+  }
+  v = bv; i = bi; s = bs;
+}
+
 // splits K at most 16 ways), then summed in split order.
 template <int PL>
 __global__ __launch_bounds__(256) void gate_select_kernel(
@@ -327,13 +363,7 @@ __global__ __launch_bounds__(256) void gate_select_kernel(
       const int e = lane + 64 * j;
       if (cand[j] && (sp[j] > bv || (sp[j] == bv && e < bi))) { bv = sp[j]; bi = e; bs = s[j]; }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const float os = __shfl_xor(bs, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; bs = os; }
-    }
+    wave_argmax(bv, bi, bs);
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j)
       if (lane + 64 * j == bi) cand[j] = false;
