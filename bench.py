@@ -54,6 +54,10 @@ def parse():
                     help="capture one forward in a HIP graph and time its replays")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured ceilings (streaming read, dense bf16 GEMM)")
+    ap.add_argument("--dispatch", default="",
+                    help="comma-separated hand-made dispatches of the config's T*topk rows, timed on the "
+                         "routed expert step alone (moe_expert_ffn): 'even' = every expert the same rows, "
+                         "an integer d = experts alternately d rows below and above that")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -269,6 +273,40 @@ def cpu_baseline(layer, ntok):
                       f"experts and the shared expert), {dt:.1f} s"}
 
 
+def hand_dispatch(a, torch, moe, inputs):
+    """The routed expert step on hand-made dispatches (random distinct tokens per
+    expert), one JSON line each: how the up and down launches respond to the
+    rows per expert, with the layer's weights and T."""
+    cfg = inputs.config_by_name(a.config)
+    layer = inputs.draw_layer(cfg)
+    dw = moe.upload_layer(layer)
+    p = moe.Params.from_config(cfg)
+    ws = moe.alloc_workspace(p, cfg.T)
+    x = moe.to_device(layer.x, cfg.act_dtype)
+    R = cfg.T * cfg.topk
+    avg = R // cfg.E
+    rng = np.random.default_rng(7)
+    for spec in a.dispatch.split(","):
+        d = 0 if spec == "even" else int(spec)
+        counts = [avg - d if e % 2 == 0 else avg + d for e in range(cfg.E)]
+        counts[-1] += R - sum(counts)
+        st = np.concatenate([np.sort(rng.choice(cfg.T, size=c, replace=False)) for c in counts]).astype(np.int32)
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        st_d, off_d = torch.from_numpy(st).cuda(), torch.from_numpy(off).cuda()
+        out = torch.empty((R, cfg.dim), dtype=p.act_torch, device="cuda")
+        for _ in range(a.warmup):
+            moe.moe_expert_ffn(p, x, st_d, off_d, dw, ws, out=out)
+        torch.cuda.synchronize()
+        moe.moe_profile_start(a.steps)
+        for _ in range(a.steps):
+            moe.moe_expert_ffn(p, x, st_d, off_d, dw, ws, out=out)
+        torch.cuda.synchronize()
+        n, up, dn = moe.moe_profile_stop()
+        print(json.dumps({"workload": cfg.name, "dispatch": spec, "rows_min": min(counts),
+                          "rows_max": max(counts), "up_ms": round(up / n, 4),
+                          "down_ms": round(dn / n, 4)}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -287,6 +325,9 @@ def main():
         return
     from mixture_experts_layer_11_amd import inputs, moe
     moe.lib()
+    if a.dispatch:
+        hand_dispatch(a, torch, moe, inputs)
+        return
     peaks = None if a.no_peaks else measured_peaks(torch, moe)
     cfg = inputs.config_by_name(a.config)
     experts = tuple(int(v) for v in a.experts.split(":")) if a.experts else None

@@ -87,14 +87,35 @@ struct TileInfo {
 // bm when bm < 32), the last one taking the remainder: m-tiles of one expert
 // then take about the same time and stream its weight slices together, so the
 // second reads them from L2.
+// With split_shared the routed tiles and the shared expert's tiles are split
+// over the 8 XCDs separately, each XCD taking an equal contiguous share of
+// both.  One range over the whole order puts all the shared expert's tiles -
+// full-height m-tiles, where routed m-tiles average fewer rows - on the last
+// XCD, which then has 7-16 % more sub-tiles to multiply than the others on
+// the prefill workloads.  That pays where a tile's time follows its rows (the
+// fp8 up launch: 3.21 -> 2.97 ms on the 8192-token layer; the 256-token bf16
+// up tiles: about 1 %), not where it follows its weight bytes (the
+// 128 x 512 bf16 up tiles: 3.22 -> 3.29 ms).  The grid needs up to two more
+// workgroups per XCD.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ sched,
                                           const int32_t* __restrict__ offsets, int E, int ntok,
-                                          int bm, TileInfo& ti) {
+                                          int bm, TileInfo& ti, bool split_shared = false) {
   const int total = sched[E + 1];
-  const int n8 = (total + 7) & ~7;
-  if ((int)blockIdx.x >= n8) return false;
-  const int tile = xcd_remap(blockIdx.x, n8);
-  if (tile >= total) return false;
+  int tile;
+  if (split_shared) {
+    const int Sr = sched[E], Ss = total - Sr;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int r0 = (int)((long)Sr * x / 8), r1 = (int)((long)Sr * (x + 1) / 8);
+    const int s0 = (int)((long)Ss * x / 8), s1 = (int)((long)Ss * (x + 1) / 8);
+    if (j < r1 - r0) tile = r0 + j;
+    else if (j - (r1 - r0) < s1 - s0) tile = Sr + s0 + j - (r1 - r0);
+    else return false;
+  } else {
+    const int n8 = (total + 7) & ~7;
+    if ((int)blockIdx.x >= n8) return false;
+    tile = xcd_remap(blockIdx.x, n8);
+    if (tile >= total) return false;
+  }
   int lo = 0, hi = E + 1;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -498,7 +519,7 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
                 "the combine tile fits in the token buffers");
   TileInfo ti;
   const int32_t* sched = p.sched + (kUp ? 0 : kComb ? 2 : 1) * (p.E + 2);
-  if (!find_tile(sched, p.offsets, p.E, p.ntok, C::BM, ti)) return;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, C::BM, ti, kUp && C::BM == SHuge::BM)) return;
   static_assert(!kComb || C::BM <= C::THREADS, "one thread stages each token's slots");
   SlotLoad sl;                                      // the tokens' routing, loaded under the K loop
   if constexpr (kComb) slots_issue(p.comb, ti.m0, ti.mrows, sl);
@@ -785,7 +806,7 @@ void stream_fp8_kernel(FfnProblem p) {
   static_assert(!kComb || F8::BM <= F8::THREADS, "one thread stages each token's slots");
   TileInfo ti;
   const int32_t* sched = p.sched + (kUp ? 0 : kComb ? 2 : 1) * (p.E + 2);
-  if (!find_tile(sched, p.offsets, p.E, p.ntok, F8::BM, ti)) return;
+  if (!find_tile(sched, p.offsets, p.E, p.ntok, F8::BM, ti, kUp)) return;
   const bool shared = ti.g == p.E;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = kUp ? p.dim : (shared ? p.inter_s : p.inter), KB = K / 128;
@@ -1250,6 +1271,7 @@ static FfnPlan plan_ffn(const FfnProblem& p) {
   L.nt_dn_s = comb_cfg ? ceil_div(p.dim, SComb::BN) : L.nt_dn;
   const long Rr = p.routed ? R : 0;
   L.g_up = Rr || p.shared_up ? round8(max_tiles(Rr, p.E, p.ntok, p.shared_up, L.bm, L.nt_up, L.nt_up_s)) : 0;
+  if (L.g_up) L.g_up += 16;   // the split of routed and shared tiles over the XCDs (find_tile)
   const bool dn_store = p.shared_down == SharedDown::Store;
   L.g_dn = Rr || dn_store ? round8(max_tiles(Rr, p.E, p.ntok, dn_store, L.bm_dn, L.nt_dn, L.nt_dn)) : 0;
   L.g_dn_s = p.shared_down == SharedDown::Combine ? round8((long)ceil_div(p.ntok, L.bm_s) * L.nt_dn_s) : 0;
