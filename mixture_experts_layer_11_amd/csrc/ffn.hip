@@ -422,7 +422,7 @@ __device__ __forceinline__ f32x16_t mma32(f32x16_t c, uint4 a, uint4 b) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <class C, int MT>
+template <class C, int MT, bool kNTW = C::NTW>
 __device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const StreamSrc<C>& S, int nk,
                                              f32x16_t (&acc)[C::NA][C::MT]) {
   const int lane = threadIdx.x & 63, fr = lane & 31, fg = lane >> 5;
@@ -437,7 +437,7 @@ __device__ __forceinline__ void stream_kloop(char (&sx)[C::NB][C::LDS], const St
 #pragma unroll
       for (int s = 0; s < C::KS; ++s) {   // k-step s: bytes 32s + 16*(lane/32) of the 2*BK-byte slice
         const char* a = S.w[j] + ((kt * 2 * C::BK + 32 * s) >> 6) * kChunkStride + (s & 1) * 512;
-        dst[j][s] = C::NTW ? ldg16_stream(a) : ldg16(a);
+        dst[j][s] = kNTW ? ldg16_stream(a) : ldg16(a);
       }
   };
   auto xload = [&](uint4 (&dst)[C::XLOADS], int kt) {
@@ -591,9 +591,20 @@ __device__ __forceinline__ void stream_tile(FfnProblem& p, char (&sx)[C::NB][C::
   const int nk = K / C::BK;
   // the K loop is instantiated for every sub-tile count, so no MFMA or token
   // load is spent on 32-row sub-tiles past the tile's last row
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((m_active == I + 1 ? stream_kloop<C, I + 1>(sx, S, nk, acc) : void()), ...);
-  }(std::make_integer_sequence<int, C::MT>{});
+  // In the 128 x 512 up tiles a routed expert of one m-tile reads each
+  // weight slice exactly once, so its weights go through non-temporal loads;
+  // experts of several m-tiles share the slices through L2 and keep ordinary
+  // loads (per tile: c2 up 3.18 -> 3.15 ms; for every tile it was slower)
+  constexpr bool kNtSingle = kUp && std::is_same_v<C, SBigUp>;
+  if (kNtSingle && ti.g < p.E && ti.M <= C::BM) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((m_active == I + 1 ? stream_kloop<C, I + 1, true>(sx, S, nk, acc) : void()), ...);
+    }(std::make_integer_sequence<int, C::MT>{});
+  } else {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((m_active == I + 1 ? stream_kloop<C, I + 1>(sx, S, nk, acc) : void()), ...);
+    }(std::make_integer_sequence<int, C::MT>{});
+  }
   if constexpr (kComb) {
     constexpr int LD = comb_ld<C::BM, C::BN>();
     uint16_t* st = reinterpret_cast<uint16_t*>(&sx[0][0]);
